@@ -1,0 +1,163 @@
+"""Benchmark of the INT8-QK / FP8-PV attention forward on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: the
+preprocessing call (K sums / V maxima, K mean and V scales, INT8 and E4M3
+codes) followed by the attention call.  The workload is the Wan-like video
+self-attention shape B=1, H=40, Nq=Nkv=32760, D=128 (tail block of 120
+tokens), Q/K/V ~ N(0,1) with one x8 outlier channel per head and a
+per-channel key bias N(0, 2^2), drawn by testkit with seed 46.  Inputs are
+resident in HBM before the timed region.
+
+Printed: one JSON line.  value = 4*B*H*Nq*Nkv*D / (time of one step), in
+TFLOP/s; attention-only and quantize-only figures, the roofline of the
+attention kernel (its average duration from HIP events recorded on the
+stream it runs on) and the CPU oracle's rate on a bounded sample are
+reported beside it.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (4·B·H·Nq·Nkv·D), INT8-QK/FP8-PV, D=128; % of MFMA peak"
+PEAK_TFLOPS = 5000.0     # MI355X dense INT8 / FP8 MFMA
+PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
+
+
+def attn_algo_bytes(B, H, Nq, Nkv):
+    """Codes + scales read and BF16 output written by one attention call."""
+    nbq, nbk = -(-Nq // 128), -(-Nkv // 128)
+    return B * H * (Nq * 128 + 2 * Nkv * 128 + 4 * (nbq + nbk + 128) + 2 * Nq * 128)
+
+
+def quant_unique_bytes(B, H, Nq, Nkv):
+    """BF16 Q/K/V read once and INT8/E4M3 codes written once."""
+    return B * H * 128 * (Nq + 2 * Nkv) * 3
+
+
+def cpu_baseline(cfg, q, k, v, rows_per_head):
+    import numpy as np
+
+    import oracle
+    t0 = time.time()
+    codes = oracle.quantize(q, k, v)
+    t_quant = time.time() - t0
+    stride = max(1, cfg.Nq // rows_per_head)
+    rows = np.array([[b, h, i] for b in range(cfg.B) for h in range(cfg.H)
+                     for i in range(0, cfg.Nq, stride)][: cfg.B * cfg.H * rows_per_head], np.int64)
+    t0 = time.time()
+    oracle.attention_rows(codes, cfg.softmax_scale, rows)
+    t_rows = time.time() - t0
+    total_rows = cfg.B * cfg.H * cfg.Nq
+    t_step = t_quant + t_rows * total_rows / len(rows)
+    return {
+        "value": cfg.flops / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"oracle quantize of the full workload ({t_quant:.2f} s) + oracle attention of "
+                   f"{len(rows)} query rows ({rows_per_head} per head, {t_rows:.2f} s), scaled to all "
+                   f"{total_rows} rows"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, help="testkit workload index")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU form in this library "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import precision_flash_attention_amd as sattn
+    import testkit
+
+    cfg = testkit.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = testkit.make_inputs(cfg)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    pbytes, wbytes = sattn.packed_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv)
+    packed = torch.empty(pbytes, dtype=torch.uint8, device=dev)
+    work = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.B, cfg.Nq, cfg.H, 128), dtype=torch.bfloat16, device=dev)
+    attend = sattn.fwd if cfg.Nq == cfg.Nkv else sattn.fwd_cross
+
+    def step():
+        p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work)
+        ev[1].record()
+        attend(p, cfg.softmax_scale, out=out)
+        return p
+
+    ev = [None, None, None]
+    for _ in range(args.warmup):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        step()
+    torch.cuda.synchronize()
+
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        step()
+        ev[2].record()
+        events.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    t_quant = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t_attn = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    t_attn_min = min(e[1].elapsed_time(e[2]) for e in events)
+
+    flops = cfg.flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tf = flops / (t_attn * 1e-3) / 1e12
+    qbytes = quant_unique_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8/fp8",
+        "data": "synthetic",
+        "config": dict(cfg.describe(), workload=cfg.name, softmax_scale=cfg.softmax_scale,
+                       step="sattn_quantize_qkv + " + ("sattn_fwd" if cfg.Nq == cfg.Nkv else "sattn_fwd_cross")),
+        "frac_of_peak": round(value / PEAK_TFLOPS, 4),
+        "attention_only": {"ms": round(t_attn, 4), "ms_min": round(t_attn_min, 4),
+                           "tflops": round(attn_tf, 2), "frac_of_peak": round(attn_tf / PEAK_TFLOPS, 4)},
+        "quantize": {"ms": round(t_quant, 4), "unique_bytes": qbytes,
+                     "gbs": round(qbytes / (t_quant * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(qbytes / (t_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tf, 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "algo_bytes": attn_algo_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_rows_per_head)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

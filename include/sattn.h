@@ -1,0 +1,149 @@
+/*
+ * sattn.h -- C ABI of libsattn: INT8-QK / FP8-PV ("SageAttention-style")
+ * dense attention forward for MI355X (gfx950).
+ *
+ * The operation.  Multi-head attention O = softmax(scale * Q K^T) V with
+ * head dimension 128, non-causal, no mask, no dropout, BF16 Q/K/V in and BF16
+ * out, computed with an INT8 Q.K^T contraction, an FP8 P.V contraction and
+ * FP32 accumulation.  This is the operand contract of the gfx1201 backend
+ * page ("[ROCm] Add aiter_sage_attn attention backend for gfx1201 (RDNA4)",
+ * section "Changes") and the INT8/FP8/BF16 row of the MI355X throughput table
+ * of "new MHA v4 entrypoint; hosts a spectrum of quantized & sparse attention
+ * kernels" (Test Result).  As on that page (Technical Details), Q/K/V
+ * preprocessing is a separate call that writes an opaque packed buffer whose
+ * size is queried first; the attention calls consume it.
+ *
+ * Quantization (the method's definition; the pages name the formats only):
+ *   - Q: per (batch, head, 128-token block) scale qs = amax|q| / 127 (FP32),
+ *     code = clamp(round-half-even(q / qs), -127, 127); qs == 0 -> codes 0.
+ *   - K: mean-smoothed.  mean[d] = (sum over 128-token blocks, in block
+ *     order, of the FP32 sum of the block's tokens in token order) / Nkv;
+ *     k' = fl32(k - mean); then per block as for Q.
+ *   - V: per (batch, head, channel) scale vs = amax|v| / 448, code = OCP
+ *     E4M3 round-to-nearest-even of clamp(v / vs, -448, 448); the sign of
+ *     zero is kept.  All divisions are correctly rounded FP32 divisions.
+ *   - Attention: S = (q8 . k8) * qs * ks * scale, online softmax in base 2,
+ *     P quantized as E4M3(448 p) against the running row maximum, O
+ *     accumulated in FP32 from FP8 P and FP8 V, row sum l from FP32 p,
+ *     O = acc * vs / (448 l) rounded to BF16.
+ *
+ * Conventions shared by every entry point.
+ *   - All device pointers are caller-owned (hipMalloc or a framework
+ *     allocator).  The library never allocates, frees or synchronizes; the
+ *     only state it keeps is a per-device architecture check.  Calls are
+ *     reentrant and stream-ordered on `stream` (a hipStream_t; NULL is the
+ *     default stream); they may be captured into a HIP graph.
+ *   - BF16 tensors are addressed as [B, N, H, 128] with element strides
+ *     (batch, sequence, head) given by a 3-entry array; the last dimension is
+ *     contiguous.  NULL strides mean contiguous BSHD (N*H*128, H*128, 128).
+ *     Base pointers must be 16-byte aligned and strides multiples of 8.
+ *   - Errors: every argument is validated before any HIP call; on error
+ *     nothing is read or written, nothing is launched and the status says
+ *     why.  There is no fallback path.  Unsupported features (D != 128, a
+ *     non-gfx950 device) are errors, never a different computation.
+ */
+#ifndef SATTN_H
+#define SATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SATTN_ABI_VERSION 1
+#define SATTN_HEAD_DIM 128
+#define SATTN_BLOCK 128
+/* longest supported sequence (keeps the K mean divisor exact in FP32) */
+#define SATTN_MAX_SEQ (1 << 24)
+
+typedef enum {
+  SATTN_OK = 0,
+  SATTN_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, size <= 0, size overflow,
+                                     bad stride, softmax_scale not finite and > 0 */
+  SATTN_ERR_UNSUPPORTED = 2,      /* D != 128; sattn_fwd with Nq != Nkv; N > SATTN_MAX_SEQ */
+  SATTN_ERR_BUFFER_TOO_SMALL = 3, /* packed or workspace bytes below the queried size */
+  SATTN_ERR_DEVICE = 4,           /* no HIP device, or the current device is not gfx950 */
+  SATTN_ERR_LAUNCH = 5            /* a kernel launch reported an error */
+} sattn_status;
+
+/* ABI version of the loaded library (SATTN_ABI_VERSION). */
+int sattn_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* sattn_status_string(sattn_status s);
+
+/*
+ * Sizes of the two caller-owned device buffers for a problem:
+ *   packed_bytes    -- output of sattn_quantize_qkv, input of the forward
+ *                      calls: Q8, K8 and V8 tiles plus all scales and the K
+ *                      mean, 256-byte aligned sections.
+ *   workspace_bytes -- scratch for the per-block K sums and V maxima
+ *                      (contents undefined between calls).
+ * Either output pointer may be NULL.  Pure host function; no device needed.
+ */
+sattn_status sattn_packed_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                size_t* packed_bytes, size_t* workspace_bytes);
+
+/*
+ * Preprocessing: quantize BF16 q [B,Nq,H,128], k and v [B,Nkv,H,128] into
+ * `packed` (the INT8/E4M3 codes in the tile order the attention kernels load
+ * into LDS, the Q/K block scales, the V channel scales and the K mean).
+ * Launches three kernels on `stream`: per-block K sums and V maxima into
+ * `workspace`; the K mean and V scales; the codes.  The result does not
+ * depend on softmax_scale, so one packed buffer serves any scale.
+ */
+sattn_status sattn_quantize_qkv(const void* q, const void* k, const void* v,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                const int64_t* q_strides, const int64_t* k_strides,
+                                const int64_t* v_strides,
+                                void* packed, size_t packed_bytes,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Self-attention forward from a packed buffer made with Nq == Nkv == N.
+ * softmax_scale: positive, finite (callers pass 1/sqrt(128) for the usual
+ * scaling).  out: BF16 [B,N,H,128] with `out_strides` (NULL = contiguous).
+ * Nq != Nkv is SATTN_ERR_UNSUPPORTED (use sattn_fwd_cross).
+ */
+sattn_status sattn_fwd(const void* packed, size_t packed_bytes,
+                       int64_t B, int64_t H, int64_t N, int64_t D, float softmax_scale,
+                       void* out, const int64_t* out_strides, void* stream);
+
+/*
+ * Cross-attention forward: any Nq, Nkv >= 1 (tuned for short key sequences
+ * such as 512 text tokens); same conventions as sattn_fwd.  The packed buffer
+ * must have been made with the same (B, H, Nq, Nkv).
+ */
+sattn_status sattn_fwd_cross(const void* packed, size_t packed_bytes,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                             float softmax_scale, void* out, const int64_t* out_strides,
+                             void* stream);
+
+/*
+ * Host-only inspection of a packed buffer (a host copy of it): writes the
+ * canonical layouts
+ *   q8 [B,H,Nq,128] int8, k8 [B,H,Nkv,128] int8, v8 [B,H,Nkv,128] E4M3 bits,
+ *   q_scale [B,H,ceil(Nq/128)], k_scale [B,H,ceil(Nkv/128)],
+ *   v_scale [B,H,128], k_mean [B,H,128] (FP32).
+ * Any output pointer may be NULL to skip it.  No device needed.
+ */
+sattn_status sattn_unpack_host(const void* packed_host, size_t packed_bytes,
+                               int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                               int8_t* q8, int8_t* k8, uint8_t* v8,
+                               float* q_scale, float* k_scale, float* v_scale, float* k_mean);
+
+/*
+ * The device FP32 -> OCP E4M3 conversion used by the V quantizer, applied
+ * elementwise: out[i] = E4M3_RNE(clamp(x[i], -448, 448)), sign of zero kept
+ * (x must not be NaN).  x: n FP32 values, out: n bytes, both device pointers;
+ * n >= 1.  Exposed so that the conversion can be checked exhaustively.
+ */
+sattn_status sattn_e4m3_encode(const float* x, uint8_t* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATTN_H */

@@ -55,6 +55,8 @@ def _load():
         lib.orc_bruteforce.restype = None
         lib.orc_rounding_mode_is_nearest.argtypes = []
         lib.orc_rounding_mode_is_nearest.restype = ctypes.c_int
+        lib.orc_num_threads.argtypes = []
+        lib.orc_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -173,3 +175,8 @@ def bruteforce(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale: float
 
 def rounding_mode_is_nearest() -> bool:
     return bool(_load().orc_rounding_mode_is_nearest())
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP regions use."""
+    return int(_load().orc_num_threads())

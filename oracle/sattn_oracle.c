@@ -31,6 +31,7 @@
 #include <string.h>
 #include <math.h>
 #include <fenv.h>
+#include <omp.h>
 
 #define D 128
 #define BLK 128
@@ -392,3 +393,14 @@ void orc_bruteforce(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 }
 
 int orc_rounding_mode_is_nearest(void) { return fegetround() == FE_TONEAREST; }
+
+/* Threads an OpenMP parallel region of this library uses. */
+int orc_num_threads(void) {
+  int n = 1;
+  #pragma omp parallel
+  {
+    #pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}

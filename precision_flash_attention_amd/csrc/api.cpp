@@ -1,0 +1,217 @@
+// api.cpp -- the C ABI of libsattn (declared in include/sattn.h): argument
+// validation, packed-buffer layout, device check and kernel launches on the
+// caller's stream.
+//
+// As the gfx1201 backend page requires of its backend ("Changes": it raises
+// on unsupported devices and on causal, mask, dropout and packed
+// multi-sequence inputs "instead of computing something else"), every call
+// validates all of its arguments before touching the device and returns an
+// error status, never a different computation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "../../include/sattn.h"
+#include "kernels.h"
+#include "layout.h"
+
+using sattn::Layout;
+
+namespace {
+
+// B*H*N*128 BF16 elements must stay below 2^40 bytes: far above any device
+// memory, and keeps every grid and index computation inside 32/64-bit ranges.
+constexpr int64_t kMaxElems = (int64_t)1 << 39;
+
+sattn_status check_dims(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0) return SATTN_ERR_INVALID_ARGUMENT;
+  if (D != SATTN_HEAD_DIM) return SATTN_ERR_UNSUPPORTED;
+  if (Nq > SATTN_MAX_SEQ || Nkv > SATTN_MAX_SEQ) return SATTN_ERR_UNSUPPORTED;
+  if (B > kMaxElems || H > kMaxElems) return SATTN_ERR_INVALID_ARGUMENT;
+  const int64_t bh = B * H;  // both <= 2^39 but the product may overflow
+  if (B != 0 && bh / B != H) return SATTN_ERR_INVALID_ARGUMENT;
+  const int64_t nmax = Nq > Nkv ? Nq : Nkv;
+  const int64_t rows = (sattn::nblocks(nmax) * SATTN_BLOCK);
+  if (bh > kMaxElems / (rows * SATTN_HEAD_DIM)) return SATTN_ERR_INVALID_ARGUMENT;
+  return SATTN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// strides: NULL = contiguous BSHD; otherwise non-negative multiples of 8.
+sattn_status get_strides(const int64_t* s, int64_t N, int64_t H, int64_t out[3]) {
+  if (s == nullptr) {
+    out[0] = N * H * SATTN_HEAD_DIM;
+    out[1] = H * SATTN_HEAD_DIM;
+    out[2] = SATTN_HEAD_DIM;
+    return SATTN_OK;
+  }
+  for (int i = 0; i < 3; ++i) {
+    if (s[i] < 0 || (s[i] % 8) != 0 || s[i] > kMaxElems) return SATTN_ERR_INVALID_ARGUMENT;
+    out[i] = s[i];
+  }
+  return SATTN_OK;
+}
+
+// Per-device result of the gfx950 check: 0 unknown, 1 ok, 2 not gfx950.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+
+sattn_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SATTN_ERR_DEVICE;
+  const char* forced = getenv("SATTN_TEST_FORCE_ARCH");  // error-path tests only
+  if (forced != nullptr) return strncmp(forced, "gfx950", 6) == 0 ? SATTN_OK : SATTN_ERR_DEVICE;
+  if (dev >= kMaxDevices) return SATTN_ERR_DEVICE;
+  int st = g_arch[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SATTN_ERR_DEVICE;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? SATTN_OK : SATTN_ERR_DEVICE;
+}
+
+sattn_status launch_status(hipError_t e) { return e == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH; }
+
+sattn_status fwd_common(const void* packed, size_t packed_bytes, int64_t B, int64_t H, int64_t Nq,
+                        int64_t Nkv, int64_t D, float softmax_scale, void* out,
+                        const int64_t* out_strides, void* stream, bool cross) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  if (packed == nullptr || out == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(packed) || !aligned16(out)) return SATTN_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return SATTN_ERR_INVALID_ARGUMENT;
+  sattn::AttnArgs a;
+  s = get_strides(out_strides, Nq, H, a.o_str);
+  if (s != SATTN_OK) return s;
+  a.L = sattn::make_layout(B, H, Nq, Nkv);
+  if (packed_bytes < a.L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
+  s = check_device();
+  if (s != SATTN_OK) return s;
+  a.packed = static_cast<const uint8_t*>(packed);
+  a.softmax_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  return launch_status(sattn::launch_attention(a, cross, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sattn_abi_version(void) { return SATTN_ABI_VERSION; }
+
+const char* sattn_status_string(sattn_status s) {
+  switch (s) {
+    case SATTN_OK: return "ok";
+    case SATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SATTN_ERR_UNSUPPORTED: return "unsupported";
+    case SATTN_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case SATTN_ERR_DEVICE: return "no gfx950 device";
+    case SATTN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+sattn_status sattn_packed_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                size_t* packed_bytes, size_t* workspace_bytes) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  const Layout L = sattn::make_layout(B, H, Nq, Nkv);
+  if (packed_bytes) *packed_bytes = L.packed_bytes;
+  if (workspace_bytes) *workspace_bytes = L.workspace_bytes;
+  return SATTN_OK;
+}
+
+sattn_status sattn_quantize_qkv(const void* q, const void* k, const void* v,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                const int64_t* q_strides, const int64_t* k_strides,
+                                const int64_t* v_strides,
+                                void* packed, size_t packed_bytes,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  if (!q || !k || !v || !packed || !workspace) return SATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(packed) || !aligned16(workspace))
+    return SATTN_ERR_INVALID_ARGUMENT;
+  sattn::QuantArgs a;
+  if ((s = get_strides(q_strides, Nq, H, a.q_str)) != SATTN_OK) return s;
+  if ((s = get_strides(k_strides, Nkv, H, a.k_str)) != SATTN_OK) return s;
+  if ((s = get_strides(v_strides, Nkv, H, a.v_str)) != SATTN_OK) return s;
+  a.L = sattn::make_layout(B, H, Nq, Nkv);
+  if (packed_bytes < a.L.packed_bytes || workspace_bytes < a.L.workspace_bytes)
+    return SATTN_ERR_BUFFER_TOO_SMALL;
+  s = check_device();
+  if (s != SATTN_OK) return s;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.packed = static_cast<uint8_t*>(packed);
+  a.workspace = static_cast<uint8_t*>(workspace);
+  return launch_status(sattn::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+sattn_status sattn_fwd(const void* packed, size_t packed_bytes, int64_t B, int64_t H, int64_t N,
+                       int64_t D, float softmax_scale, void* out, const int64_t* out_strides,
+                       void* stream) {
+  return fwd_common(packed, packed_bytes, B, H, N, N, D, softmax_scale, out, out_strides, stream,
+                    false);
+}
+
+sattn_status sattn_fwd_cross(const void* packed, size_t packed_bytes, int64_t B, int64_t H,
+                             int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale, void* out,
+                             const int64_t* out_strides, void* stream) {
+  return fwd_common(packed, packed_bytes, B, H, Nq, Nkv, D, softmax_scale, out, out_strides,
+                    stream, true);
+}
+
+sattn_status sattn_unpack_host(const void* packed_host, size_t packed_bytes, int64_t B, int64_t H,
+                               int64_t Nq, int64_t Nkv, int64_t D, int8_t* q8, int8_t* k8,
+                               uint8_t* v8, float* q_scale, float* k_scale, float* v_scale,
+                               float* k_mean) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  if (packed_host == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
+  const Layout L = sattn::make_layout(B, H, Nq, Nkv);
+  if (packed_bytes < L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
+  const uint8_t* P = static_cast<const uint8_t*>(packed_host);
+  const int64_t BH = B * H;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    if (q8)
+      for (int64_t n = 0; n < Nq; ++n) {
+        const uint8_t* tile = P + L.off_q8 + (bh * L.nbq + n / 128) * sattn::kTileBytes;
+        for (int c = 0; c < 128; ++c)
+          q8[(bh * Nq + n) * 128 + c] = (int8_t)tile[sattn::q_pos((int)(n % 128), c)];
+      }
+    if (k8)
+      for (int64_t n = 0; n < Nkv; ++n) {
+        const uint8_t* tile = P + L.off_k8 + (bh * L.nbk + n / 128) * sattn::kTileBytes;
+        for (int c = 0; c < 128; ++c)
+          k8[(bh * Nkv + n) * 128 + c] = (int8_t)tile[sattn::k_pos((int)(n % 128), c)];
+      }
+    if (v8)
+      for (int64_t n = 0; n < Nkv; ++n) {
+        const uint8_t* tile = P + L.off_v8 + (bh * L.nbk + n / 128) * sattn::kTileBytes;
+        for (int d = 0; d < 128; ++d) v8[(bh * Nkv + n) * 128 + d] = tile[sattn::v_pos((int)(n % 128), d)];
+      }
+  }
+  if (q_scale) memcpy(q_scale, P + L.off_qs, (size_t)BH * L.nbq * 4);
+  if (k_scale) memcpy(k_scale, P + L.off_ks, (size_t)BH * L.nbk * 4);
+  if (v_scale) memcpy(v_scale, P + L.off_vs, (size_t)BH * 128 * 4);
+  if (k_mean) memcpy(k_mean, P + L.off_km, (size_t)BH * 128 * 4);
+  return SATTN_OK;
+}
+
+sattn_status sattn_e4m3_encode(const float* x, uint8_t* out, int64_t n, void* stream) {
+  if (x == nullptr || out == nullptr || n <= 0 || n > kMaxElems) return SATTN_ERR_INVALID_ARGUMENT;
+  sattn_status s = check_device();
+  if (s != SATTN_OK) return s;
+  return launch_status(sattn::launch_e4m3_encode(x, out, n, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// kernels.h -- launchers implemented in the .hip translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace sattn {
+
+struct QuantArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t q_str[3], k_str[3], v_str[3];  // element strides (batch, seq, head)
+  Layout L;
+  uint8_t* packed;
+  uint8_t* workspace;
+};
+
+struct AttnArgs {
+  const uint8_t* packed;
+  Layout L;
+  float softmax_scale;
+  uint16_t* out;
+  int64_t o_str[3];
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream);
+hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace sattn

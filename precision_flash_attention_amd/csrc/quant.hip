@@ -1,0 +1,344 @@
+// quant.hip -- preprocessing kernels: BF16 Q/K/V -> INT8 / OCP E4M3 codes.
+//
+// The MHA v4 page ("new MHA v4 entrypoint ...", Technical Details) keeps Q/K/V
+// preprocessing apart from the attention kernel and its import listing names
+// a two-stage per-channel V amax (partial kernel, finalize kernel, quantize
+// kernel).  Here the same three stages serve both K and V:
+//   1. stats:    per (b, h, 128-token block, channel) the FP32 sum of K over
+//                the block's tokens in token order, and the max |V|.
+//   2. finalize: per (b, h, channel) the K mean (block sums added in block
+//                order, one division by Nkv) and the V scale amax/448.
+//   3. codes:    per (b, h, block) Q and mean-smoothed K to INT8 with scale
+//                amax/127 and round-half-even; V to E4M3 with its channel
+//                scale, written transposed in the attention kernel's order.
+//
+// The codes must equal those of the plain definition bit for bit, where the
+// quotient x / s is one correctly rounded FP32 division.  A full division
+// costs about ten VALU operations, more than an HBM-bound kernel can spend
+// per element, so the kernels form y = x * fl(1/s) (within 2^-23 relative of
+// x / s) and fall back to the exact division only when y lies so close to a
+// rounding boundary that the two could round differently.  Build with
+// -ffp-contract=off.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "layout.h"
+
+namespace sattn {
+namespace {
+
+constexpr float kFltMin = 1.17549435e-38f;  // 2^-126
+
+__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ inline void unpack8(const uint4& u, float f[8]) {
+  f[0] = lo_bf16(u.x); f[1] = hi_bf16(u.x);
+  f[2] = lo_bf16(u.y); f[3] = hi_bf16(u.y);
+  f[4] = lo_bf16(u.z); f[5] = hi_bf16(u.z);
+  f[6] = lo_bf16(u.w); f[7] = hi_bf16(u.w);
+}
+
+// ------------------------------------------------------------- 1. stats ----
+// One thread per (b, block t, head, 8-channel group): consecutive threads
+// read consecutive 16-byte pieces of one token row, so a wave reads 1 KiB
+// contiguous per token of a contiguous BSHD tensor.
+struct StatsP {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t ks0, ks1, ks2, vs0, vs1, vs2;
+  int64_t B, H, Nkv, nbk;
+  float* kpart;
+  float* vpart;
+};
+
+__global__ __launch_bounds__(256) void k_stats(StatsP p) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = p.B * p.nbk * p.H * 16;
+  if (tid >= total) return;
+  const int g = (int)(tid & 15);
+  int64_t r = tid >> 4;
+  const int64_t h = r % p.H;
+  r /= p.H;
+  const int64_t t = r % p.nbk;
+  const int64_t b = r / p.nbk;
+  const int64_t n0 = t * kBlk;
+  const int64_t n1 = n0 + kBlk < p.Nkv ? n0 + kBlk : p.Nkv;
+  const uint16_t* kp = p.k + b * p.ks0 + h * p.ks2 + 8 * g;
+  const uint16_t* vp = p.v + b * p.vs0 + h * p.vs2 + 8 * g;
+  float s[8], m[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { s[c] = 0.0f; m[c] = 0.0f; }
+  int64_t n = n0;
+  // batches of 8 tokens: the loads are issued together, the adds stay in
+  // token order
+  for (; n + 8 <= n1; n += 8) {
+    uint4 kk[8], vv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kk[i] = *reinterpret_cast<const uint4*>(kp + (n + i) * p.ks1);
+      vv[i] = *reinterpret_cast<const uint4*>(vp + (n + i) * p.vs1);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float kf[8], vf[8];
+      unpack8(kk[i], kf);
+      unpack8(vv[i], vf);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        s[c] = s[c] + kf[c];
+        m[c] = fmaxf(m[c], fabsf(vf[c]));
+      }
+    }
+  }
+  for (; n < n1; ++n) {
+    float kf[8], vf[8];
+    unpack8(*reinterpret_cast<const uint4*>(kp + n * p.ks1), kf);
+    unpack8(*reinterpret_cast<const uint4*>(vp + n * p.vs1), vf);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s[c] = s[c] + kf[c];
+      m[c] = fmaxf(m[c], fabsf(vf[c]));
+    }
+  }
+  const int64_t o = ((b * p.H + h) * p.nbk + t) * kD + 8 * g;
+  float4* ko = reinterpret_cast<float4*>(p.kpart + o);
+  float4* vo = reinterpret_cast<float4*>(p.vpart + o);
+  ko[0] = make_float4(s[0], s[1], s[2], s[3]);
+  ko[1] = make_float4(s[4], s[5], s[6], s[7]);
+  vo[0] = make_float4(m[0], m[1], m[2], m[3]);
+  vo[1] = make_float4(m[4], m[5], m[6], m[7]);
+}
+
+// ---------------------------------------------------------- 2. finalize ----
+struct FinP {
+  const float* kpart;
+  const float* vpart;
+  int64_t BH, nbk, Nkv;
+  float* k_mean;
+  float* v_scale;
+};
+
+__global__ __launch_bounds__(128) void k_finalize(FinP p) {
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* kp = p.kpart + bh * p.nbk * kD + d;
+  const float* vp = p.vpart + bh * p.nbk * kD + d;
+  float tot = 0.0f, m = 0.0f;
+  for (int64_t t = 0; t < p.nbk; ++t) {
+    tot = tot + kp[t * kD];
+    m = fmaxf(m, vp[t * kD]);
+  }
+  p.k_mean[bh * kD + d] = __fdiv_rn(tot, (float)p.Nkv);
+  p.v_scale[bh * kD + d] = __fdiv_rn(m, 448.0f);
+}
+
+// ------------------------------------------------------------- 3. codes ----
+
+// clamp(RNE(x / s), -127, 127), s > 0.  `r` = fl(1/s), `exact` when s is
+// subnormal (then fl(1/s) may overflow and x*r is no longer within 2^-23).
+__device__ inline int int8_code(float x, float s, float r, bool exact) {
+  float y = exact ? __fdiv_rn(x, s) : x * r;
+  float t = __builtin_rintf(y);
+  // |y - x/s| <= 2^-16 for |x/s| <= 128, and fl(x/s) is within 2^-17 of
+  // x/s: unless y is within 2^-15 of a half-integer both round alike.
+  if (!exact && fabsf(y - t) > 0.499969482421875f) t = __builtin_rintf(__fdiv_rn(x, s));
+  t = fminf(fmaxf(t, -127.0f), 127.0f);
+  return (int)t;
+}
+
+__device__ inline float clamp448(float y) { return fminf(fmaxf(y, -448.0f), 448.0f); }
+
+// Hardware FP32 -> OCP E4M3, round to nearest even, for |y| <= 448.
+__device__ inline uint32_t e4m3_hw(float y) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFFu;
+}
+
+// E4M3(clamp(v / s, +-448)), s > 0.  The exact quotient lies between
+// y(1 - 2^-20) and y(1 + 2^-20); rounding is monotone, so when both ends give
+// the same code that code is the answer.
+__device__ inline uint32_t e4m3_code(float v, float s, float r, bool exact) {
+  if (exact) return e4m3_hw(clamp448(__fdiv_rn(v, s)));
+  const float y = v * r;
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+      clamp448(y * 0.99999904632568359375f), clamp448(y * 1.00000095367431640625f), 0, false);
+  if ((w & 0xFFu) == ((w >> 8) & 0xFFu)) return w & 0xFFu;
+  return e4m3_hw(clamp448(__fdiv_rn(v, s)));
+}
+
+__device__ inline float wave_max(float a) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+  return a;
+}
+
+struct CodeP {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2;
+  int64_t H, Nq, Nkv, nbq, nbk, BH;
+  uint8_t* q8;
+  uint8_t* k8;
+  uint8_t* v8;
+  float* q_scale;
+  float* k_scale;
+  const float* v_scale;
+  const float* k_mean;
+};
+
+// One workgroup of 256 threads per (tensor, b, h, 128-token block).  Thread
+// (tg, cg) holds tokens 8tg..8tg+7 x channels 8cg..8cg+7 of the block.
+__global__ __launch_bounds__(256) void k_codes(CodeP p) {
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kTileBytes];
+  __shared__ float red[4];
+  const int64_t wid = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int tg = tid >> 4, cg = tid & 15;
+  int kind;  // 0 = Q, 1 = K, 2 = V
+  int64_t bh, t;
+  if (wid < p.BH * p.nbq) { kind = 0; bh = wid / p.nbq; t = wid % p.nbq; }
+  else if (wid < p.BH * (p.nbq + p.nbk)) { kind = 1; int64_t u = wid - p.BH * p.nbq; bh = u / p.nbk; t = u % p.nbk; }
+  else { kind = 2; int64_t u = wid - p.BH * (p.nbq + p.nbk); bh = u / p.nbk; t = u % p.nbk; }
+  const int64_t b = bh / p.H, h = bh % p.H;
+  const int64_t N = kind == 0 ? p.Nq : p.Nkv;
+  const uint16_t* src;
+  int64_t s0, s1, s2;
+  if (kind == 0) { src = p.q; s0 = p.qs0; s1 = p.qs1; s2 = p.qs2; }
+  else if (kind == 1) { src = p.k; s0 = p.ks0; s1 = p.ks1; s2 = p.ks2; }
+  else { src = p.v; s0 = p.vs0; s1 = p.vs1; s2 = p.vs2; }
+  const uint16_t* base = src + b * s0 + h * s2 + 8 * cg;
+  const int64_t n_base = t * kBlk + 8 * tg;
+
+  float x[8][8];
+  bool valid[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    valid[i] = n_base + i < N;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (valid[i]) u = *reinterpret_cast<const uint4*>(base + (n_base + i) * s1);
+    unpack8(u, x[i]);
+  }
+
+  if (kind == 2) {
+    // ---- V: channel scales from the finalize step; E4M3 codes written into
+    // an LDS copy of the V^T tile, then copied out in 16-byte pieces.
+    float sc[8], rc[8];
+    bool ex[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      sc[c] = p.v_scale[bh * kD + 8 * cg + c];
+      ex[c] = sc[c] < kFltMin;
+      rc[c] = ex[c] ? 0.0f : __fdiv_rn(1.0f, sc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t w0 = 0, w1 = 0;
+      if (sc[c] != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t code = valid[i] ? e4m3_code(x[i][c], sc[c], rc[c], ex[c]) : 0u;
+          if (i < 4) w0 |= code << (8 * i);
+          else w1 |= code << (8 * (i - 4));
+        }
+      }
+      const int d = 8 * cg + c;
+      const int key = 8 * tg;
+      *reinterpret_cast<uint32_t*>(vt + v_pos(key, d)) = w0;
+      *reinterpret_cast<uint32_t*>(vt + v_pos(key + 4, d)) = w1;
+    }
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(p.v8 + (bh * p.nbk + t) * kTileBytes);
+    const uint4* s = reinterpret_cast<const uint4*>(vt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[tid + 256 * j] = s[tid + 256 * j];
+    return;
+  }
+
+  // ---- Q and K: block amax, scale amax/127, INT8 codes.
+  if (kind == 1) {
+    float mean[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) mean[c] = p.k_mean[bh * kD + 8 * cg + c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[i][c] = valid[i] ? x[i][c] - mean[c] : 0.0f;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (valid[i]) am = fmaxf(am, fabsf(x[i][c]));
+  am = wave_max(am);
+  if ((tid & 63) == 0) red[tid >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(am, 127.0f);
+  const bool ex = s < kFltMin;
+  const float r = ex ? 0.0f : __fdiv_rn(1.0f, s);
+  if (tid == 0) (kind == 0 ? p.q_scale : p.k_scale)[bh * (kind == 0 ? p.nbq : p.nbk) + t] = s;
+  uint8_t* tile = (kind == 0 ? p.q8 + (bh * p.nbq + t) * kTileBytes : p.k8 + (bh * p.nbk + t) * kTileBytes);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t w[2] = {0u, 0u};
+    if (valid[i] && s != 0.0f) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t code = (uint32_t)(int8_code(x[i][c], s, r, ex) & 0xFF);
+        w[c >> 2] |= code << (8 * (c & 3));
+      }
+    }
+    const int row = 8 * tg + i;
+    const int pos = kind == 0 ? q_pos(row, 8 * cg) : k_pos(row, 8 * cg);
+    *reinterpret_cast<uint2*>(tile + pos) = make_uint2(w[0], w[1]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_e4m3(const float* x, uint8_t* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)e4m3_hw(clamp448(x[i]));
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
+  const Layout& L = a.L;
+  const int64_t BH = L.B * L.H;
+  float* kpart = reinterpret_cast<float*>(a.workspace + L.ws_kpart);
+  float* vpart = reinterpret_cast<float*>(a.workspace + L.ws_vpart);
+  float* q_scale = reinterpret_cast<float*>(a.packed + L.off_qs);
+  float* k_scale = reinterpret_cast<float*>(a.packed + L.off_ks);
+  float* v_scale = reinterpret_cast<float*>(a.packed + L.off_vs);
+  float* k_mean = reinterpret_cast<float*>(a.packed + L.off_km);
+
+  StatsP sp{a.k, a.v, a.k_str[0], a.k_str[1], a.k_str[2], a.v_str[0], a.v_str[1], a.v_str[2],
+            L.B, L.H, L.Nkv, L.nbk, kpart, vpart};
+  const int64_t sthreads = L.B * L.nbk * L.H * 16;
+  hipLaunchKernelGGL(k_stats, dim3((unsigned)((sthreads + 255) / 256)), dim3(256), 0, stream, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  FinP fp{kpart, vpart, BH, L.nbk, L.Nkv, k_mean, v_scale};
+  hipLaunchKernelGGL(k_finalize, dim3((unsigned)BH), dim3(128), 0, stream, fp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  CodeP cp{a.q, a.k, a.v,
+           a.q_str[0], a.q_str[1], a.q_str[2], a.k_str[0], a.k_str[1], a.k_str[2],
+           a.v_str[0], a.v_str[1], a.v_str[2],
+           L.H, L.Nq, L.Nkv, L.nbq, L.nbk, BH,
+           a.packed + L.off_q8, a.packed + L.off_k8, a.packed + L.off_v8,
+           q_scale, k_scale, v_scale, k_mean};
+  hipLaunchKernelGGL(k_codes, dim3((unsigned)(BH * (L.nbq + 2 * L.nbk))), dim3(256), 0, stream, cp);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t stream) {
+  hipLaunchKernelGGL(k_e4m3, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace sattn
