@@ -74,14 +74,38 @@ __device__ inline uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int QB, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnP p) {
+// MFMAs read their operands from all 64 lanes.  The epilogue stores under a
+// per-lane condition (rows past Nq), and without this fence the compiler may
+// sink the last PV MFMAs into that exec-masked region, where masked-off
+// lanes would feed wrong operands into the valid lanes' results.  The empty
+// asm "reads and rewrites" the accumulators, so they are complete before the
+// branch.
+__device__ inline void pin_accumulators(v16f (&O)[4]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(O[db]));
+}
+
+// Global -> LDS copy of one 16-byte piece per lane (global_load_lds with
+// 16-byte size, new on gfx950): lane l's piece lands at dst + 16 l, so each
+// wave instruction fills 1 KiB of LDS without passing through VGPRs.
+__device__ inline void copy_to_lds(const uint8_t* src_lane, uint8_t* dst_wave) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src_lane,
+                                   (void __attribute__((address_space(3)))*)dst_wave, 16, 0, 0);
+}
+
+// Float whose bits are 0x4B400000 + acc equals 1.5 * 2^23 + acc for
+// |acc| < 2^22; INT8 MFMA accumulators started from these bits can be read
+// as floats without a conversion.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagicF = 12582912.0f;
+
+template <int NW, bool MAGIC>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnP p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * QB * 32;
-  constexpr int NCH = 2 * (int)kTileBytes / 16 / NT;  // 16-byte pieces per thread per stage
-  static_assert(NCH * NT * 16 == kStageBytes, "stage must split evenly");
-  static_assert((1024 % NT) == 0, "K/V halves must split evenly");
+  constexpr int BM = NW * 32;
+  constexpr int kChunks = 2 * (int)kTileBytes / 16;  // 16-byte pieces per stage
+  constexpr int CPW = kChunks / NW;                  // pieces per wave
+  static_assert(CPW % 64 == 0 && 1024 % CPW == 0, "stage must split into whole wave copies");
 
   // Workgroups are dispatched round-robin over the 8 XCDs; remap so that the
   // workgroups resident on one XCD take consecutive q-tiles of the same head
@@ -97,135 +121,137 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnP p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int q0 = mtile * BM + w * QB * 32;  // first query of this wave
+  const int q0 = mtile * BM + w * 32;  // first query of this wave
   const int qblk = q0 >> 7;
 
   // ---- the wave's Q codes (B operand of S^T), resident for the whole loop
-  v4i qf[QB][4];
+  v4i qf[4];
   float qscale = 0.0f;
   if (q0 < p.nbq * 128) {
     const uint8_t* qt = p.q8 + (bh * p.nbq + qblk) * kTileBytes;
+    const v4i* src = reinterpret_cast<const v4i*>(qt + ((q0 & 127) + l32) * 128 + 64 * hh);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const v4i* src = reinterpret_cast<const v4i*>(qt + ((q0 & 127) + 32 * qb + l32) * 128 + 64 * hh);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) qf[qb][m] = src[m];
-    }
+    for (int m = 0; m < 4; ++m) qf[m] = src[m];
     qscale = p.qs[bh * p.nbq + qblk];
   } else {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) qf[qb][m] = v4i{0, 0, 0, 0};
+    for (int m = 0; m < 4; ++m) qf[m] = v4i{0, 0, 0, 0};
   }
 
   const uint8_t* kbase = p.k8 + bh * p.nbk * kTileBytes;
   const uint8_t* vbase = p.v8 + bh * p.nbk * kTileBytes;
   const float* ksc = p.ks + bh * p.nbk;
 
-  v4i stg[NCH];
-  auto gload = [&](int t) {
-    const v4i* kt = reinterpret_cast<const v4i*>(kbase + (int64_t)t * kTileBytes);
-    const v4i* vt = reinterpret_cast<const v4i*>(vbase + (int64_t)t * kTileBytes);
+  auto issue_tile = [&](int t, int stage) {
+    const uint8_t* kt = kbase + (int64_t)t * kTileBytes;
+    const uint8_t* vt = vbase + (int64_t)t * kTileBytes;
+    uint8_t* dst = smem + stage * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + j * NT;
-      stg[j] = c < 1024 ? kt[c] : vt[c - 1024];
+    for (int i = 0; i < CPW / 64; ++i) {
+      const int c0 = w * CPW + i * 64;  // wave-uniform
+      const uint8_t* src = c0 < 1024 ? kt + (c0 + lane) * 16 : vt + (c0 - 1024 + lane) * 16;
+      copy_to_lds(src, dst + c0 * 16);
     }
   };
-  auto swrite = [&](int s) {
-    v4i* dst = reinterpret_cast<v4i*>(smem + s * kStageBytes);
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) dst[tid + j * NT] = stg[j];
-  };
 
-  float m_run[QB], l_run[QB];
-  v16f O[4][QB];
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  v16f O[4];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -__builtin_inff();
-    l_run[qb] = 0.0f;
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int r = 0; r < 16; ++r) O[db][r] = 0.0f;
+  v16i S0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) O[db][qb][r] = 0.0f;
-  }
+  for (int r = 0; r < 16; ++r) S0[r] = MAGIC ? kMagicBits : 0;
 
   auto tile = [&](const uint8_t* Ks, const uint8_t* Vs, float c, int rem, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
-    // ---- S^T = K8 . Q8^T
-    v16i S[4][QB];
+    // ---- S^T = K8 . Q8^T : four 32-key blocks x four 32-channel steps.
+    // K fragments of block kb+1 are read while block kb's MFMAs run, so at
+    // most two blocks of fragments are live.
+    v16i S[4];
+    v4i kf[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int row = kb * 32 + l32;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        kf[kb][m] = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ (row & 7)) & 7) << 4));
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], S0, 0, 0, 0);
+#pragma unroll
+      for (int m = 1; m < 4; ++m) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][m], qf[m], S[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // Phase fences keep each phase's operands from being hoisted into the
+    // previous one: the second wave on the SIMD overlaps the phases instead.
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- online softmax: integer tile max (c > 0 is uniform over the tile)
+    constexpr int kMaskedVal = MAGIC ? 0x4B000000 : -(1 << 30);
+    int mx = kMaskedVal;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[kb][qb][r] = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int row = kb * 32 + l32;
-        const v4i kf = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ (row & 7)) & 7) << 4));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          S[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][m], S[kb][qb], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        if (kMasked) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= rem) S[kb][r] = kMaskedVal;
+        }
+        mx = max(mx, (int)S[kb][r]);
       }
+    mx = max(mx, other_half_i(mx));
+    const float mt = (MAGIC ? (__int_as_float(mx) - kMagicF) : (float)mx) * c;
+    const float mnew = fmaxf(m_run, mt);
+    if (__any(mnew > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
-    // ---- online softmax, P8 packing
-    uint32_t P[QB][2][8];
+    m_run = mnew;
+    // p448 = exp2(acc * c - m + log2 448); with MAGIC the float read of the
+    // biased accumulator carries 1.5 * 2^23 * c, folded into the addend
+    const float nb = MAGIC ? __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew) : kLog2_448 - mnew;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t P[2][8];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      int mx = -(1 << 30);
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int j = 0; j < 8; ++j) {
+        const int kb = 2 * g + (j >> 2);
+        const int r0 = 4 * (j & 3);
+        float pv[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int i = 0; i < 4; ++i) {
+          const float x = MAGIC ? __int_as_float(S[kb][r0 + i]) : (float)S[kb][r0 + i];
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, nb));
           if (kMasked) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= rem) S[kb][qb][r] = -(1 << 30);
+            const int key = kb * 32 + 8 * (j & 3) + 4 * hh + i;
+            if (key >= rem) pv[i] = 0.0f;
           }
-          mx = max(mx, (int)S[kb][qb][r]);
+          ls[i] += pv[i];
         }
-      mx = max(mx, other_half_i(mx));
-      const float mt = (float)mx * c;
-      const float mnew = fmaxf(m_run[qb], mt);
-      if (__any(mnew > m_run[qb])) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[db][qb][r] *= alpha;
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
+        P[g][j] = (uint32_t)wd;
       }
-      m_run[qb] = mnew;
-      const float mneg = kLog2_448 - mnew;
-      float ls = 0.0f;
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kb = 2 * g + (j >> 2);
-          const int r0 = 4 * (j & 3);
-          float pv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[kb][qb][r0 + i], c, mneg));
-            if (kMasked) {
-              const int key = kb * 32 + 8 * (j & 3) + 4 * hh + i;
-              if (key >= rem) pv[i] = 0.0f;
-            }
-            ls += pv[i];
-          }
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
-          P[qb][g][j] = (uint32_t)wd;
-        }
-      l_run[qb] += ls;
-    }
-    // ---- O^T += V8^T . P8
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V8^T . P8 (V fragments read one MFMA ahead)
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
+      const v8i Bp = {(int)P[g][0], (int)P[g][1], (int)P[g][2], (int)P[g][3],
+                      (int)P[g][4], (int)P[g][5], (int)P[g][6], (int)P[g][7]};
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int d = db * 32 + l32;
@@ -234,62 +260,332 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnP p) {
         const v4i lo = *reinterpret_cast<const v4i*>(vrow + (((ch0 ^ (d & 7)) & 7) << 4));
         const v4i hi = *reinterpret_cast<const v4i*>(vrow + ((((ch0 + 1) ^ (d & 7)) & 7) << 4));
         const v8i A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const v8i Bp = {(int)P[qb][g][0], (int)P[qb][g][1], (int)P[qb][g][2], (int)P[qb][g][3],
-                          (int)P[qb][g][4], (int)P[qb][g][5], (int)P[qb][g][6], (int)P[qb][g][7]};
-          O[db][qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bp, O[db][qb], 0, 0, 0, 127, 0, 127);
-        }
+        O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bp, O[db], 0, 0, 0, 127, 0, 127);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
 
-
-  gload(0);
-  swrite(0);
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int t = 0; t < p.nbk; ++t) {
-    if (t + 1 < p.nbk) gload(t + 1);
+  // Full tiles; stage (t+1)&1 was last read in iteration t-1, which every
+  // wave has left (barrier), so it can be refilled while tile t is consumed.
+  for (int t = 0; t + 1 < p.nbk; ++t) {
+    issue_tile(t + 1, (t + 1) & 1);
     const uint8_t* Ks = smem + (t & 1) * kStageBytes;
-    const uint8_t* Vs = Ks + kTileBytes;
+    tile(Ks, Ks + kTileBytes, qscale * ksc[t] * p.sl2e, 128, std::false_type{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  {
+    // the last tile, masked when the sequence ends inside it; peeled so the
+    // loop body carries no masking state
+    const int t = p.nbk - 1;
+    const uint8_t* Ks = smem + (t & 1) * kStageBytes;
     const float c = qscale * ksc[t] * p.sl2e;
     const int rem = p.Nkv - t * 128;
-    if (rem >= 128) tile(Ks, Vs, c, rem, std::false_type{});
-    else tile(Ks, Vs, c, rem, std::true_type{});
-    if (t + 1 < p.nbk) swrite((t + 1) & 1);
-    __syncthreads();
+    if (rem >= 128) tile(Ks, Ks + kTileBytes, c, rem, std::false_type{});
+    else tile(Ks, Ks + kTileBytes, c, rem, std::true_type{});
   }
 
   // ---- epilogue: O = acc * vs / l448 -> BF16
+  pin_accumulators(O);
   const float* vsc = p.vs + bh * 128;
+  const float lt = l_run + other_half_f(l_run);
+  const int q = q0 + l32;
+  if (q < p.Nq) {
+    const float inv = 1.0f / lt;
+    uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l_run[qb] + other_half_f(l_run[qb]);
-    const int q = q0 + 32 * qb + l32;
-    if (q < p.Nq) {
-      const float inv = 1.0f / lt;
-      uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int d0 = 32 * db + 8 * a + 4 * hh;
-          const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
-          const float o0 = O[db][qb][4 * a + 0] * sv.x * inv;
-          const float o1 = O[db][qb][4 * a + 1] * sv.y * inv;
-          const float o2 = O[db][qb][4 * a + 2] * sv.z * inv;
-          const float o3 = O[db][qb][4 * a + 3] * sv.w * inv;
-          *reinterpret_cast<uint2*>(orow + d0) =
-              make_uint2(bf16_rne(o0) | (bf16_rne(o1) << 16), bf16_rne(o2) | (bf16_rne(o3) << 16));
-        }
-    }
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * db + 8 * a + 4 * hh;
+        const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
+        const float o0 = O[db][4 * a + 0] * sv.x * inv;
+        const float o1 = O[db][4 * a + 1] * sv.y * inv;
+        const float o2 = O[db][4 * a + 2] * sv.z * inv;
+        const float o3 = O[db][4 * a + 3] * sv.w * inv;
+        *reinterpret_cast<uint2*>(orow + d0) =
+            make_uint2(bf16_rne(o0) | (bf16_rne(o1) << 16), bf16_rne(o2) | (bf16_rne(o3) << 16));
+      }
   }
 }
 
-template <int QB, int NW>
-hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// Ping-pong variant: 8 waves, 32 queries each.  Waves w and w+4 share a SIMD.
+// Group A (waves 0-3) runs one barrier slot ahead of group B (waves 4-7), so
+// in every slot one wave of each SIMD issues MFMAs while its partner runs the
+// softmax on the VALU:
+//     slot    2t          2t+1        2t+2
+//     A       M(t)        V(t)        M(t+1)
+//     B       V(t-1)      M(t)        V(t)
+// M(t) = O += V(t-1)^T . P(t-1) followed by S(t) = K(t) . Q^T;
+// V(t) = online softmax of S(t) -> P(t), with the conditional O rescale.
+// Tile u lives in LDS stage u % 3 from slot 2u (K read by A) to slot 2u+3
+// (V read by B); group A loads tile t+1 at the start of M(t) and waits for
+// it at the end of V(t).
+template <bool MAGIC, bool PRIO>
+__global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int NW = 8;
+  constexpr int BM = NW * 32;
+
+  const int64_t G8 = (p.G + 7) / 8 * 8;
+  const int64_t wg = blockIdx.x;
+  const int64_t L = (wg % 8) * (G8 / 8) + wg / 8;
+  if (L >= p.G) return;
+  const int64_t bh = L / p.mt;
+  const int mtile = (int)(L % p.mt);
+  const int64_t b = bh / p.H, h = bh % p.H;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // the wave index through readfirstlane: a scalar, so every branch on the
+  // wave's group (and the barriers inside them) is a scalar branch
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const bool isA = w < 4;
+  const int q0 = mtile * BM + w * 32;
+  const int qblk = q0 >> 7;
+  const int nbk = p.nbk;
+
+  v4i qf[4];
+  float qscale = 0.0f;
+  if (q0 < p.nbq * 128) {
+    const uint8_t* qt = p.q8 + (bh * p.nbq + qblk) * kTileBytes;
+    const v4i* src = reinterpret_cast<const v4i*>(qt + ((q0 & 127) + l32) * 128 + 64 * hh);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qf[m] = src[m];
+    qscale = p.qs[bh * p.nbq + qblk];
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qf[m] = v4i{0, 0, 0, 0};
+  }
+
+  const uint8_t* kbase = p.k8 + bh * nbk * kTileBytes;
+  const uint8_t* vbase = p.v8 + bh * nbk * kTileBytes;
+  const float* ksc = p.ks + bh * nbk;
+
+  // copy tile t into stage `stage` using `nwaves` waves starting at wave `w0`
+  auto copy_tile = [&](int t, int stage, int widx, int nwaves) {
+    const uint8_t* kt = kbase + (int64_t)t * kTileBytes;
+    const uint8_t* vt = vbase + (int64_t)t * kTileBytes;
+    uint8_t* dst = smem + stage * kStageBytes;
+    const int per = 2048 / nwaves;  // 16-byte pieces per wave
+    for (int i = 0; i < per / 64; ++i) {
+      const int c0 = widx * per + i * 64;
+      const uint8_t* src = c0 < 1024 ? kt + (c0 + lane) * 16 : vt + (c0 - 1024 + lane) * 16;
+      copy_to_lds(src, dst + c0 * 16);
+    }
+  };
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  v16f O[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[db][r] = 0.0f;
+  v16i S[4];
+  uint32_t P[2][8];
+  v16i S0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S0[r] = MAGIC ? kMagicBits : 0;
+  float c_cur = 0.0f;  // dequant scale of the tile whose S is held
+
+  // ---- M(t): PV of tile t-1, then S of tile t
+  auto mblock = [&](int t, bool do_pv, bool do_s) {
+    // the MFMA-issuing wave of the SIMD gets issue priority over its partner
+    if (PRIO) __builtin_amdgcn_s_setprio(2);
+    if (isA && t >= 1 && t + 1 < nbk) copy_tile(t + 1, (t + 1) % 3, w, 4);
+    if (do_pv) {
+      const uint8_t* Vs = smem + ((t + 2) % 3) * kStageBytes + kTileBytes;  // stage of t-1
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const v8i Bp = {(int)P[g][0], (int)P[g][1], (int)P[g][2], (int)P[g][3],
+                        (int)P[g][4], (int)P[g][5], (int)P[g][6], (int)P[g][7]};
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = db * 32 + l32;
+          const uint8_t* vrow = Vs + d * 128;
+          const int ch0 = 4 * g + 2 * hh;
+          const v4i lo = *reinterpret_cast<const v4i*>(vrow + (((ch0 ^ (d & 7)) & 7) << 4));
+          const v4i hi = *reinterpret_cast<const v4i*>(vrow + ((((ch0 + 1) ^ (d & 7)) & 7) << 4));
+          const v8i A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bp, O[db], 0, 0, 0, 127, 0, 127);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if (do_s) {
+      const uint8_t* Ks = smem + (t % 3) * kStageBytes;
+      v4i kf[4][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int row = kb * 32 + l32;
+          kf[kb][m] = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ (row & 7)) & 7) << 4));
+        }
+      // m-outer: the four accumulation chains (one per key block) interleave,
+      // so no MFMA waits on the result of the one just issued
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], S0, 0, 0, 0);
+#pragma unroll
+      for (int m = 1; m < 4; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][m], qf[m], S[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      c_cur = qscale * ksc[t] * p.sl2e;
+    }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- V(t): online softmax of S -> P, conditional rescale of O
+  auto vblock = [&](int rem, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    const float c = c_cur;
+    constexpr int kMaskedVal = MAGIC ? 0x4B000000 : -(1 << 30);
+    int mx = kMaskedVal;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (kMasked) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= rem) S[kb][r] = kMaskedVal;
+        }
+        mx = max(mx, (int)S[kb][r]);
+      }
+    mx = max(mx, other_half_i(mx));
+    const float mt = (MAGIC ? (__int_as_float(mx) - kMagicF) : (float)mx) * c;
+    const float mnew = fmaxf(m_run, mt);
+    if (__any(mnew > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    }
+    m_run = mnew;
+    const float nb = MAGIC ? __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew) : kLog2_448 - mnew;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kb = 2 * g + (j >> 2);
+        const int r0 = 4 * (j & 3);
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = MAGIC ? __int_as_float(S[kb][r0 + i]) : (float)S[kb][r0 + i];
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, nb));
+          if (kMasked) {
+            const int key = kb * 32 + 8 * (j & 3) + 4 * hh + i;
+            if (key >= rem) pv[i] = 0.0f;
+          }
+          ls[i] += pv[i];
+        }
+        // the first conversion writes the low half only: start from the
+        // register's old contents instead of materialising a zero
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], (int)P[g][j], false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
+        P[g][j] = (uint32_t)wd;
+      }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  auto barrier = [] { __builtin_amdgcn_s_barrier(); };
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) P[g][j] = 0u;
+
+  // prologue: tiles 0 and 1 into stages 0 and 1, all waves copying
+  copy_tile(0, 0, w, 8);
+  if (nbk > 1) copy_tile(1, 1, w, 8);
+  wait_loads();
+  __syncthreads();
+
+  if (!isA) barrier();  // group B lags one slot
+  const int last = nbk - 1;
+  const int rem = p.Nkv - last * 128;
+  int t = 0;
+  for (; t < last; ++t) {
+    mblock(t, t > 0, true);
+    barrier();
+    vblock(128, std::false_type{});
+    if (isA) wait_loads();
+    barrier();
+  }
+  mblock(last, last > 0, true);
+  barrier();
+  if (rem >= 128) vblock(rem, std::false_type{});
+  else vblock(rem, std::true_type{});
+  if (isA) wait_loads();
+  barrier();
+  mblock(nbk, true, false);
+  if (isA) barrier();
+
+  // ---- epilogue: O = acc * vs / l448 -> BF16
+  pin_accumulators(O);
+  const float* vsc = p.vs + bh * 128;
+  const float lt = l_run + other_half_f(l_run);
+  const int q = q0 + l32;
+  if (q < p.Nq) {
+    const float inv = 1.0f / lt;
+    uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * db + 8 * a + 4 * hh;
+        const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
+        const float o0 = O[db][4 * a + 0] * sv.x * inv;
+        const float o1 = O[db][4 * a + 1] * sv.y * inv;
+        const float o2 = O[db][4 * a + 2] * sv.z * inv;
+        const float o3 = O[db][4 * a + 3] * sv.w * inv;
+        *reinterpret_cast<uint2*>(orow + d0) =
+            make_uint2(bf16_rne(o0) | (bf16_rne(o1) << 16), bf16_rne(o2) | (bf16_rne(o3) << 16));
+      }
+  }
+}
+
+template <bool MAGIC, bool PRIO>
+hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
-  constexpr int BM = NW * QB * 32;
+  constexpr int BM = 256;
+  constexpr int kLds = 3 * kStageBytes;
+  static bool attr_set = false;  // raising the dynamic LDS limit is per function, once
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<MAGIC, PRIO>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   AttnP p;
   p.q8 = a.packed + L.off_q8;
   p.k8 = a.packed + L.off_k8;
@@ -310,7 +606,35 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
   p.G = L.B * L.H * p.mt;
   p.sl2e = a.softmax_scale * kLog2e;
   const int64_t G8 = (p.G + 7) / 8 * 8;
-  hipLaunchKernelGGL((attn_fwd_kernel<QB, NW>), dim3((unsigned)G8), dim3(NW * 64), kStageBytes * 2, stream, p);
+  hipLaunchKernelGGL((attn_pp_kernel<MAGIC, PRIO>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
+  return hipGetLastError();
+}
+
+template <int NW, bool MAGIC>
+hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
+  const Layout& L = a.L;
+  constexpr int BM = NW * 32;
+  AttnP p;
+  p.q8 = a.packed + L.off_q8;
+  p.k8 = a.packed + L.off_k8;
+  p.v8 = a.packed + L.off_v8;
+  p.qs = reinterpret_cast<const float*>(a.packed + L.off_qs);
+  p.ks = reinterpret_cast<const float*>(a.packed + L.off_ks);
+  p.vs = reinterpret_cast<const float*>(a.packed + L.off_vs);
+  p.out = a.out;
+  p.os0 = a.o_str[0];
+  p.os1 = a.o_str[1];
+  p.os2 = a.o_str[2];
+  p.H = (int)L.H;
+  p.Nq = (int)L.Nq;
+  p.Nkv = (int)L.Nkv;
+  p.nbq = (int)L.nbq;
+  p.nbk = (int)L.nbk;
+  p.mt = (int)((L.Nq + BM - 1) / BM);
+  p.G = L.B * L.H * p.mt;
+  p.sl2e = a.softmax_scale * kLog2e;
+  const int64_t G8 = (p.G + 7) / 8 * 8;
+  hipLaunchKernelGGL((attn_fwd_kernel<NW, MAGIC>), dim3((unsigned)G8), dim3(NW * 64), kStageBytes * 2, stream, p);
   return hipGetLastError();
 }
 
@@ -318,7 +642,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
   (void)cross;
-  return launch_cfg<1, 4>(a, stream);
+  return launch_pp<true, false>(a, stream);
 }
 
 }  // namespace sattn
