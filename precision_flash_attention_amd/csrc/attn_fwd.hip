@@ -176,7 +176,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnP p) {
       const int row = kb * 32 + l32;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        kf[kb][m] = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ (row & 7)) & 7) << 4));
+        kf[kb][m] = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ swz(row)) & 7) << 4));
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -257,8 +257,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnP p) {
         const int d = db * 32 + l32;
         const uint8_t* vrow = Vs + d * 128;
         const int ch0 = 4 * g + 2 * hh;
-        const v4i lo = *reinterpret_cast<const v4i*>(vrow + (((ch0 ^ (d & 7)) & 7) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(vrow + ((((ch0 + 1) ^ (d & 7)) & 7) << 4));
+        const v4i lo = *reinterpret_cast<const v4i*>(vrow + (((ch0 ^ swz(d)) & 7) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(vrow + ((((ch0 + 1) ^ swz(d)) & 7) << 4));
         const v8i A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bp, O[db], 0, 0, 0, 127, 0, 127);
       }
@@ -416,8 +416,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
           const int d = db * 32 + l32;
           const uint8_t* vrow = Vs + d * 128;
           const int ch0 = 4 * g + 2 * hh;
-          const v4i lo = *reinterpret_cast<const v4i*>(vrow + (((ch0 ^ (d & 7)) & 7) << 4));
-          const v4i hi = *reinterpret_cast<const v4i*>(vrow + ((((ch0 + 1) ^ (d & 7)) & 7) << 4));
+          const v4i lo = *reinterpret_cast<const v4i*>(vrow + (((ch0 ^ swz(d)) & 7) << 4));
+          const v4i hi = *reinterpret_cast<const v4i*>(vrow + ((((ch0 + 1) ^ swz(d)) & 7) << 4));
           const v8i A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bp, O[db], 0, 0, 0, 127, 0, 127);
         }
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const int row = kb * 32 + l32;
-          kf[kb][m] = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ (row & 7)) & 7) << 4));
+          kf[kb][m] = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ swz(row)) & 7) << 4));
         }
       // m-outer: the four accumulation chains (one per key block) interleave,
       // so no MFMA waits on the result of the one just issued
@@ -642,7 +642,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
   (void)cross;
-  return launch_pp<true, false>(a, stream);
+  return launch_pp<true, true>(a, stream);
 }
 
 }  // namespace sattn

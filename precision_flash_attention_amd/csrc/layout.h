@@ -10,14 +10,16 @@
 //        (token, channel); rows past Nq are zero.  Loaded straight into
 //        registers as the B operand of the K.Q^T MFMA.
 //   k8   [B][H][nbk] tiles, row-major (key, channel) with the 16-byte chunk
-//        index XOR-ed with (key & 7) so that eight lanes reading the same
-//        logical chunk of eight consecutive keys hit eight different LDS
-//        bank groups.  Rows past Nkv are zero.
+//        index XOR-ed with ((key >> 1) & 7).  gfx950's LDS serves a 16-byte
+//        read for 16 lanes per cycle across 64 banks (256 bytes); sixteen
+//        lanes reading the same logical chunk of sixteen consecutive keys
+//        then hit sixteen different 16-byte bank groups (row r starts at
+//        bank group 8(r & 1)).  Rows past Nkv are zero.
 //   v8   [B][H][nbk] tiles of V^T: row = channel d (128 rows), 128 key
 //        columns.  Inside each group of 64 keys the columns follow the
 //        k-index order of the FP8 MFMA B operand as the K.Q^T accumulator
 //        leaves P in registers (see v_col below), so P never moves between
-//        lanes; the 16-byte chunks are XOR-swizzled with (d & 7).
+//        lanes; the 16-byte chunks are XOR-swizzled with ((d >> 1) & 7).
 //        Columns of keys past Nkv are zero.
 //   q_scale [B][H][nbq], k_scale [B][H][nbk], v_scale [B][H][128],
 //   k_mean  [B][H][128]  (FP32)
@@ -75,8 +77,11 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv) {
 // Byte offset of (token r, channel c) inside a Q tile.
 SATTN_HD inline int q_pos(int r, int c) { return r * 128 + c; }
 
+// XOR pattern of the 16-byte chunks of a K or V^T tile row.
+SATTN_HD inline int swz(int row) { return (row >> 1) & 7; }
+
 // Byte offset of (key r, channel c) inside a K tile.
-SATTN_HD inline int k_pos(int r, int c) { return r * 128 + ((((c >> 4) ^ (r & 7)) & 7) << 4) + (c & 15); }
+SATTN_HD inline int k_pos(int r, int c) { return r * 128 + ((((c >> 4) ^ swz(r)) & 7) << 4) + (c & 15); }
 
 // Column of key j (0..127) inside a V^T tile row.  Within a 64-key group the
 // K.Q^T accumulator of the 32x32 INT8 MFMA gives lane half hh the keys
@@ -93,7 +98,7 @@ SATTN_HD inline int v_col(int j) {
 // Byte offset of (key j, channel d) inside a V^T tile.
 SATTN_HD inline int v_pos(int j, int d) {
   const int col = v_col(j);
-  return d * 128 + ((((col >> 4) ^ (d & 7)) & 7) << 4) + (col & 15);
+  return d * 128 + ((((col >> 4) ^ swz(d)) & 7) << 4) + (col & 15);
 }
 
 }  // namespace sattn
