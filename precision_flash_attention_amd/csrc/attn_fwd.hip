@@ -8,10 +8,10 @@
 // softmax rescale is conditional (skipped for a wave when no row maximum of
 // the tile grew), the exponentials run on the VALU in base 2 (log2(e) folded
 // into the dequantisation scale), and MFMA, VALU and loads are overlapped
-// (two LDS stages: the next K/V tile is fetched while the current one is
-// consumed).
+// (two groups of waves alternate MFMA and softmax phases; K/V tiles stream
+// into three LDS stages by LDS-DMA while earlier tiles are consumed).
 //
-// Data flow per wave (QB blocks of 32 queries; 128-key tiles):
+// Data flow per wave (32 queries; 128-key tiles):
 //   S^T = K8 . Q8^T   v_mfma_i32_32x32x32_i8, A = K tile rows from LDS,
 //                     B = the wave's Q codes held in VGPRs for the whole
 //                     kernel.  The accumulator leaves each lane one query
@@ -86,11 +86,13 @@ __device__ inline void pin_accumulators(v16f (&O)[4]) {
 }
 
 // Global -> LDS copy of one 16-byte piece per lane (global_load_lds with
-// 16-byte size, new on gfx950): lane l's piece lands at dst + 16 l, so each
-// wave instruction fills 1 KiB of LDS without passing through VGPRs.
-__device__ inline void copy_to_lds(const uint8_t* src_lane, uint8_t* dst_wave) {
+// 16-byte size, new on gfx950): lane l's piece lands at dst + OFF + 16 l, so
+// each wave instruction fills 1 KiB of LDS without passing through VGPRs.
+// OFF (the instruction's immediate offset) is added to both addresses.
+template <int OFF>
+__device__ inline void copy_to_lds_off(const uint8_t* src_lane, uint8_t* dst_wave) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src_lane,
-                                   (void __attribute__((address_space(3)))*)dst_wave, 16, 0, 0);
+                                   (void __attribute__((address_space(3)))*)dst_wave, 16, OFF, 0);
 }
 
 // Float whose bits are 0x4B400000 + acc equals 1.5 * 2^23 + acc for
@@ -99,228 +101,8 @@ __device__ inline void copy_to_lds(const uint8_t* src_lane, uint8_t* dst_wave) {
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagicF = 12582912.0f;
 
-template <int NW, bool MAGIC>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnP p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int BM = NW * 32;
-  constexpr int kChunks = 2 * (int)kTileBytes / 16;  // 16-byte pieces per stage
-  constexpr int CPW = kChunks / NW;                  // pieces per wave
-  static_assert(CPW % 64 == 0 && 1024 % CPW == 0, "stage must split into whole wave copies");
-
-  // Workgroups are dispatched round-robin over the 8 XCDs; remap so that the
-  // workgroups resident on one XCD take consecutive q-tiles of the same head
-  // and share its K/V tiles in that XCD's L2.
-  const int64_t G8 = (p.G + 7) / 8 * 8;
-  const int64_t wg = blockIdx.x;
-  const int64_t L = (wg % 8) * (G8 / 8) + wg / 8;
-  if (L >= p.G) return;
-  const int64_t bh = L / p.mt;
-  const int mtile = (int)(L % p.mt);
-  const int64_t b = bh / p.H, h = bh % p.H;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int q0 = mtile * BM + w * 32;  // first query of this wave
-  const int qblk = q0 >> 7;
-
-  // ---- the wave's Q codes (B operand of S^T), resident for the whole loop
-  v4i qf[4];
-  float qscale = 0.0f;
-  if (q0 < p.nbq * 128) {
-    const uint8_t* qt = p.q8 + (bh * p.nbq + qblk) * kTileBytes;
-    const v4i* src = reinterpret_cast<const v4i*>(qt + ((q0 & 127) + l32) * 128 + 64 * hh);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) qf[m] = src[m];
-    qscale = p.qs[bh * p.nbq + qblk];
-  } else {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) qf[m] = v4i{0, 0, 0, 0};
-  }
-
-  const uint8_t* kbase = p.k8 + bh * p.nbk * kTileBytes;
-  const uint8_t* vbase = p.v8 + bh * p.nbk * kTileBytes;
-  const float* ksc = p.ks + bh * p.nbk;
-
-  auto issue_tile = [&](int t, int stage) {
-    const uint8_t* kt = kbase + (int64_t)t * kTileBytes;
-    const uint8_t* vt = vbase + (int64_t)t * kTileBytes;
-    uint8_t* dst = smem + stage * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < CPW / 64; ++i) {
-      const int c0 = w * CPW + i * 64;  // wave-uniform
-      const uint8_t* src = c0 < 1024 ? kt + (c0 + lane) * 16 : vt + (c0 - 1024 + lane) * 16;
-      copy_to_lds(src, dst + c0 * 16);
-    }
-  };
-
-  float m_run = -__builtin_inff(), l_run = 0.0f;
-  v16f O[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) O[db][r] = 0.0f;
-  v16i S0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) S0[r] = MAGIC ? kMagicBits : 0;
-
-  auto tile = [&](const uint8_t* Ks, const uint8_t* Vs, float c, int rem, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    // ---- S^T = K8 . Q8^T : four 32-key blocks x four 32-channel steps.
-    // K fragments of block kb+1 are read while block kb's MFMAs run, so at
-    // most two blocks of fragments are live.
-    v16i S[4];
-    v4i kf[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        kf[kb][m] = *reinterpret_cast<const v4i*>(Ks + row * 128 + ((((4 * hh + m) ^ swz(row)) & 7) << 4));
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], S0, 0, 0, 0);
-#pragma unroll
-      for (int m = 1; m < 4; ++m) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][m], qf[m], S[kb], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    // Phase fences keep each phase's operands from being hoisted into the
-    // previous one: the second wave on the SIMD overlaps the phases instead.
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- online softmax: integer tile max (c > 0 is uniform over the tile)
-    constexpr int kMaskedVal = MAGIC ? 0x4B000000 : -(1 << 30);
-    int mx = kMaskedVal;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kMasked) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= rem) S[kb][r] = kMaskedVal;
-        }
-        mx = max(mx, (int)S[kb][r]);
-      }
-    mx = max(mx, other_half_i(mx));
-    const float mt = (MAGIC ? (__int_as_float(mx) - kMagicF) : (float)mx) * c;
-    const float mnew = fmaxf(m_run, mt);
-    if (__any(mnew > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
-    }
-    m_run = mnew;
-    // p448 = exp2(acc * c - m + log2 448); with MAGIC the float read of the
-    // biased accumulator carries 1.5 * 2^23 * c, folded into the addend
-    const float nb = MAGIC ? __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew) : kLog2_448 - mnew;
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    uint32_t P[2][8];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kb = 2 * g + (j >> 2);
-        const int r0 = 4 * (j & 3);
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = MAGIC ? __int_as_float(S[kb][r0 + i]) : (float)S[kb][r0 + i];
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, nb));
-          if (kMasked) {
-            const int key = kb * 32 + 8 * (j & 3) + 4 * hh + i;
-            if (key >= rem) pv[i] = 0.0f;
-          }
-          ls[i] += pv[i];
-        }
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wd, true);
-        P[g][j] = (uint32_t)wd;
-      }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V8^T . P8 (V fragments read one MFMA ahead)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const v8i Bp = {(int)P[g][0], (int)P[g][1], (int)P[g][2], (int)P[g][3],
-                      (int)P[g][4], (int)P[g][5], (int)P[g][6], (int)P[g][7]};
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + l32;
-        const uint8_t* vrow = Vs + d * 128;
-        const int ch0 = 4 * g + 2 * hh;
-        const v4i lo = *reinterpret_cast<const v4i*>(vrow + (((ch0 ^ swz(d)) & 7) << 4));
-        const v4i hi = *reinterpret_cast<const v4i*>(vrow + ((((ch0 + 1) ^ swz(d)) & 7) << 4));
-        const v8i A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bp, O[db], 0, 0, 0, 127, 0, 127);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 7; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  };
-
-  issue_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  // Full tiles; stage (t+1)&1 was last read in iteration t-1, which every
-  // wave has left (barrier), so it can be refilled while tile t is consumed.
-  for (int t = 0; t + 1 < p.nbk; ++t) {
-    issue_tile(t + 1, (t + 1) & 1);
-    const uint8_t* Ks = smem + (t & 1) * kStageBytes;
-    tile(Ks, Ks + kTileBytes, qscale * ksc[t] * p.sl2e, 128, std::false_type{});
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  {
-    // the last tile, masked when the sequence ends inside it; peeled so the
-    // loop body carries no masking state
-    const int t = p.nbk - 1;
-    const uint8_t* Ks = smem + (t & 1) * kStageBytes;
-    const float c = qscale * ksc[t] * p.sl2e;
-    const int rem = p.Nkv - t * 128;
-    if (rem >= 128) tile(Ks, Ks + kTileBytes, c, rem, std::false_type{});
-    else tile(Ks, Ks + kTileBytes, c, rem, std::true_type{});
-  }
-
-  // ---- epilogue: O = acc * vs / l448 -> BF16
-  pin_accumulators(O);
-  const float* vsc = p.vs + bh * 128;
-  const float lt = l_run + other_half_f(l_run);
-  const int q = q0 + l32;
-  if (q < p.Nq) {
-    const float inv = 1.0f / lt;
-    uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * db + 8 * a + 4 * hh;
-        const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
-        const float o0 = O[db][4 * a + 0] * sv.x * inv;
-        const float o1 = O[db][4 * a + 1] * sv.y * inv;
-        const float o2 = O[db][4 * a + 2] * sv.z * inv;
-        const float o3 = O[db][4 * a + 3] * sv.w * inv;
-        *reinterpret_cast<uint2*>(orow + d0) =
-            make_uint2(bf16_rne(o0) | (bf16_rne(o1) << 16), bf16_rne(o2) | (bf16_rne(o3) << 16));
-      }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Ping-pong variant: 8 waves, 32 queries each.  Waves w and w+4 share a SIMD.
+// 8 waves, 32 queries each.  Waves w and w+4 share a SIMD.
 // Group A (waves 0-3) runs one barrier slot ahead of group B (waves 4-7), so
 // in every slot one wave of each SIMD issues MFMAs while its partner runs the
 // softmax on the VALU:
@@ -374,16 +156,22 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   const uint8_t* vbase = p.v8 + bh * nbk * kTileBytes;
   const float* ksc = p.ks + bh * nbk;
 
-  // copy tile t into stage `stage` using `nwaves` waves starting at wave `w0`
+  // Copy tile t into stage `stage`: wave `widx` of `nwaves` copies a
+  // contiguous 32/nwaves KiB piece (within the K or the V^T tile).  The LDS
+  // destination base lives in M0, and rewriting M0 waits for the previous
+  // LDS-DMA to have consumed it, so M0 is set once per 4 KiB and the
+  // instruction's immediate offset (added to both addresses) steps by 1 KiB.
   auto copy_tile = [&](int t, int stage, int widx, int nwaves) {
-    const uint8_t* kt = kbase + (int64_t)t * kTileBytes;
-    const uint8_t* vt = vbase + (int64_t)t * kTileBytes;
-    uint8_t* dst = smem + stage * kStageBytes;
     const int per = 2048 / nwaves;  // 16-byte pieces per wave
-    for (int i = 0; i < per / 64; ++i) {
-      const int c0 = widx * per + i * 64;
-      const uint8_t* src = c0 < 1024 ? kt + (c0 + lane) * 16 : vt + (c0 - 1024 + lane) * 16;
-      copy_to_lds(src, dst + c0 * 16);
+    const int c0 = widx * per;      // first piece, wave-uniform
+    const uint8_t* src = (c0 < 1024 ? kbase + (int64_t)t * kTileBytes + c0 * 16
+                                    : vbase + (int64_t)t * kTileBytes + (c0 - 1024) * 16) + lane * 16;
+    uint8_t* dst = smem + stage * kStageBytes + c0 * 16;
+    for (int i = 0; i < per / 256; ++i) {
+      copy_to_lds_off<0>(src + i * 4096, dst + i * 4096);
+      copy_to_lds_off<1024>(src + i * 4096, dst + i * 4096);
+      copy_to_lds_off<2048>(src + i * 4096, dst + i * 4096);
+      copy_to_lds_off<3072>(src + i * 4096, dst + i * 4096);
     }
   };
 
@@ -399,6 +187,12 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) S0[r] = MAGIC ? kMagicBits : 0;
   float c_cur = 0.0f;  // dequant scale of the tile whose S is held
+  // The K block scales are read through the constant address space, which
+  // makes these uniform loads scalar (s_load, counted by lgkmcnt).  A vector
+  // load here would be followed by a vmcnt wait that also waits for the
+  // LDS-DMA of the next tile issued in the same block.
+  const __attribute__((address_space(4))) float* ksc4 =
+      (const __attribute__((address_space(4))) float*)(ksc);
 
   // ---- M(t): PV of tile t-1, then S of tile t
   auto mblock = [&](int t, bool do_pv, bool do_s) {
@@ -455,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      c_cur = qscale * ksc[t] * p.sl2e;
+      c_cur = qscale * ksc4[t] * p.sl2e;
     }
     if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
@@ -607,34 +401,6 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   p.sl2e = a.softmax_scale * kLog2e;
   const int64_t G8 = (p.G + 7) / 8 * 8;
   hipLaunchKernelGGL((attn_pp_kernel<MAGIC, PRIO>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
-  return hipGetLastError();
-}
-
-template <int NW, bool MAGIC>
-hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
-  const Layout& L = a.L;
-  constexpr int BM = NW * 32;
-  AttnP p;
-  p.q8 = a.packed + L.off_q8;
-  p.k8 = a.packed + L.off_k8;
-  p.v8 = a.packed + L.off_v8;
-  p.qs = reinterpret_cast<const float*>(a.packed + L.off_qs);
-  p.ks = reinterpret_cast<const float*>(a.packed + L.off_ks);
-  p.vs = reinterpret_cast<const float*>(a.packed + L.off_vs);
-  p.out = a.out;
-  p.os0 = a.o_str[0];
-  p.os1 = a.o_str[1];
-  p.os2 = a.o_str[2];
-  p.H = (int)L.H;
-  p.Nq = (int)L.Nq;
-  p.Nkv = (int)L.Nkv;
-  p.nbq = (int)L.nbq;
-  p.nbk = (int)L.nbk;
-  p.mt = (int)((L.Nq + BM - 1) / BM);
-  p.G = L.B * L.H * p.mt;
-  p.sl2e = a.softmax_scale * kLog2e;
-  const int64_t G8 = (p.G + 7) / 8 * 8;
-  hipLaunchKernelGGL((attn_fwd_kernel<NW, MAGIC>), dim3((unsigned)G8), dim3(NW * 64), kStageBytes * 2, stream, p);
   return hipGetLastError();
 }
 
