@@ -15,6 +15,7 @@ stream it runs on) and the CPU oracle's rate on a bounded sample are
 reported beside it.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -27,6 +28,14 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s (4·B·H·Nq·Nkv·D), INT8-QK/FP8-PV, D=128; % of MFMA peak"
 PEAK_TFLOPS = 5000.0     # MI355X dense INT8 / FP8 MFMA
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
+ATTN_KERNEL = "attn_pp_kernel"
+# Sources that fix the attention kernel's code; the committed traffic record
+# is used only while their digest matches the one it was measured with.
+ATTN_SOURCES = ("precision_flash_attention_amd/csrc/attn_fwd.hip",
+                "precision_flash_attention_amd/csrc/layout.h",
+                "precision_flash_attention_amd/csrc/kernels.h")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_pp_kernel_wan_b1h40n32760_traffic.md")
+COPY_BYTES = 1 << 30
 
 
 def attn_algo_bytes(B, H, Nq, Nkv):
@@ -38,6 +47,42 @@ def attn_algo_bytes(B, H, Nq, Nkv):
 def quant_unique_bytes(B, H, Nq, Nkv):
     """BF16 Q/K/V read once and INT8/E4M3 codes written once."""
     return B * H * 128 * (Nq + 2 * Nkv) * 3
+
+
+def attn_kernel_digest():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed FETCH_SIZE and
+    WRITE_SIZE passes, each scaled by what the same counter read for a plain
+    device copy of COPY_BYTES; None when there is no record for this workload
+    or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            line = next(ln for ln in fh if ln.startswith("traffic-record: "))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line[len("traffic-record: "):])
+    if rec.get("kernel_digest") != attn_kernel_digest() or rec.get("workload") != workload:
+        return None
+    fetch = rec["fetch_kib"] * rec["copy_bytes"] / rec["copy_fetch_kib"]
+    write = rec["write_kib"] * rec["copy_bytes"] / rec["copy_write_kib"]
+    return int(round(fetch + write))
+
+
+def copy_calibration(torch, dev):
+    """Plain device-to-device copies of a known size, for scaling the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(cfg, q, k, v, rows_per_head):
@@ -74,6 +119,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="testkit workload index")
     ap.add_argument("--cpu-rows-per-head", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 1 GiB device copies (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path has no multi-GPU form in this library "
@@ -149,11 +196,14 @@ def main():
         "quantize": {"ms": round(t_quant, 4), "unique_bytes": qbytes,
                      "gbs": round(qbytes / (t_quant * 1e-3) / 1e9, 1),
                      "frac_of_hbm_peak": round(qbytes / (t_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tf, 2),
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(attn_tf, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_TFLOPS, 4),
-                     "traffic": None,
-                     "algo_bytes": attn_algo_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv)},
+                     "traffic": measured_traffic(cfg.name),
+                     "algo_bytes": attn_algo_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv),
+                     "kernel_digest": attn_kernel_digest()},
     }
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_rows_per_head)
     print(json.dumps(rec), flush=True)

@@ -57,12 +57,17 @@ extern "C" {
 #define SATTN_BLOCK 128
 /* longest supported sequence (keeps the K mean divisor exact in FP32) */
 #define SATTN_MAX_SEQ (1 << 24)
+/* largest B * H * ceil(max(Nq, Nkv) / 128): keeps every launch's grid within
+   32-bit work-item counts (2^22 blocks are 2^36 elements per tensor, more
+   than one GPU's memory holds) */
+#define SATTN_MAX_BLOCKS (1 << 22)
 
 typedef enum {
   SATTN_OK = 0,
   SATTN_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, size <= 0, size overflow,
                                      bad stride, softmax_scale not finite and > 0 */
-  SATTN_ERR_UNSUPPORTED = 2,      /* D != 128; sattn_fwd with Nq != Nkv; N > SATTN_MAX_SEQ */
+  SATTN_ERR_UNSUPPORTED = 2,      /* D != 128; sattn_fwd with Nq != Nkv; N > SATTN_MAX_SEQ;
+                                     more than SATTN_MAX_BLOCKS blocks */
   SATTN_ERR_BUFFER_TOO_SMALL = 3, /* packed or workspace bytes below the queried size */
   SATTN_ERR_DEVICE = 4,           /* no HIP device, or the current device is not gfx950 */
   SATTN_ERR_LAUNCH = 5            /* a kernel launch reported an error */

@@ -37,6 +37,7 @@ sattn_status check_dims(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D
   const int64_t nmax = Nq > Nkv ? Nq : Nkv;
   const int64_t rows = (sattn::nblocks(nmax) * SATTN_BLOCK);
   if (bh > kMaxElems / (rows * SATTN_HEAD_DIM)) return SATTN_ERR_INVALID_ARGUMENT;
+  if (bh * sattn::nblocks(nmax) > SATTN_MAX_BLOCKS) return SATTN_ERR_UNSUPPORTED;
   return SATTN_OK;
 }
 

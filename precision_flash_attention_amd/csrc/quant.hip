@@ -120,18 +120,55 @@ struct FinP {
   float* v_scale;
 };
 
-__global__ __launch_bounds__(128) void k_finalize(FinP p) {
+// One workgroup per (b, h, 32-channel group).  The block partials are staged
+// through LDS 64 blocks at a time (the next chunk's loads are in flight while
+// the current one is summed), so the serial FP32 sum over blocks waits on LDS,
+// not on one HBM round trip per block.
+constexpr int kFinChunk = 64;
+
+__global__ __launch_bounds__(256) void k_finalize(FinP p) {
+  __shared__ float sk[kFinChunk][32];
+  __shared__ float sv[kFinChunk][32];
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* kp = p.kpart + bh * p.nbk * kD + d;
-  const float* vp = p.vpart + bh * p.nbk * kD + d;
+  const int c0 = 32 * (int)blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* kp = p.kpart + bh * p.nbk * kD + c0;
+  const float* vp = p.vpart + bh * p.nbk * kD + c0;
+  float4 rk[2], rv[2];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i;
+      const int64_t t = t0 + (idx >> 3);
+      const int c = 4 * (idx & 7);
+      rk[i] = rv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (t < p.nbk) {
+        rk[i] = *reinterpret_cast<const float4*>(kp + t * kD + c);
+        rv[i] = *reinterpret_cast<const float4*>(vp + t * kD + c);
+      }
+    }
+  };
   float tot = 0.0f, m = 0.0f;
-  for (int64_t t = 0; t < p.nbk; ++t) {
-    tot = tot + kp[t * kD];
-    m = fmaxf(m, vp[t * kD]);
+  fetch(0);
+  for (int64_t t0 = 0; t0 < p.nbk; t0 += kFinChunk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i;
+      *reinterpret_cast<float4*>(&sk[idx >> 3][4 * (idx & 7)]) = rk[i];
+      *reinterpret_cast<float4*>(&sv[idx >> 3][4 * (idx & 7)]) = rv[i];
+    }
+    __syncthreads();
+    fetch(t0 + kFinChunk);
+    const int cnt = (int)(p.nbk - t0 < kFinChunk ? p.nbk - t0 : kFinChunk);
+    if (tid < 32) {
+      for (int t = 0; t < cnt; ++t) tot = tot + sk[t][tid];
+    } else if (tid < 64) {
+      for (int t = 0; t < cnt; ++t) m = fmaxf(m, sv[t][tid - 32]);
+    }
+    __syncthreads();
   }
-  p.k_mean[bh * kD + d] = __fdiv_rn(tot, (float)p.Nkv);
-  p.v_scale[bh * kD + d] = __fdiv_rn(m, 448.0f);
+  if (tid < 32) p.k_mean[bh * kD + c0 + tid] = __fdiv_rn(tot, (float)p.Nkv);
+  else if (tid < 64) p.v_scale[bh * kD + c0 + tid - 32] = __fdiv_rn(m, 448.0f);
 }
 
 // ------------------------------------------------------------- 3. codes ----
@@ -197,11 +234,27 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
   const int tid = threadIdx.x;
   const int tg = tid >> 4, cg = tid & 15;
   int kind;  // 0 = Q, 1 = K, 2 = V
-  int64_t bh, t;
-  if (wid < p.BH * p.nbq) { kind = 0; bh = wid / p.nbq; t = wid % p.nbq; }
-  else if (wid < p.BH * (p.nbq + p.nbk)) { kind = 1; int64_t u = wid - p.BH * p.nbq; bh = u / p.nbk; t = u % p.nbk; }
-  else { kind = 2; int64_t u = wid - p.BH * (p.nbq + p.nbk); bh = u / p.nbk; t = u % p.nbk; }
-  const int64_t b = bh / p.H, h = bh % p.H;
+  int64_t b, h, t;
+  const int64_t nkv = p.BH * p.nbk;
+  if (wid < 2 * nkv) {
+    // K and V blocks first, alternating, in the reverse of the order the
+    // stats step read them ((b, t, h) ascending): the blocks it read last
+    // are the likeliest to still sit in the memory-side cache.
+    kind = 1 + (int)(wid & 1);
+    int64_t r = nkv - 1 - (wid >> 1);
+    h = r % p.H;
+    r /= p.H;
+    t = r % p.nbk;
+    b = r / p.nbk;
+  } else {
+    kind = 0;
+    const int64_t u = wid - 2 * nkv;
+    const int64_t bq = u / p.nbq;
+    t = u % p.nbq;
+    b = bq / p.H;
+    h = bq % p.H;
+  }
+  const int64_t bh = b * p.H + h;
   const int64_t N = kind == 0 ? p.Nq : p.Nkv;
   const uint16_t* src;
   int64_t s0, s1, s2;
@@ -322,7 +375,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
 
   FinP fp{kpart, vpart, BH, L.nbk, L.Nkv, k_mean, v_scale};
-  hipLaunchKernelGGL(k_finalize, dim3((unsigned)BH), dim3(128), 0, stream, fp);
+  hipLaunchKernelGGL(k_finalize, dim3((unsigned)BH, 4), dim3(256), 0, stream, fp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -66,6 +66,10 @@ def test_packed_bytes_errors(lib):
     assert lib.sattn_packed_bytes(1, 1, (1 << 24) + 1, 128, 128, ctypes.byref(pb), None) == UNSUPPORTED
     assert lib.sattn_packed_bytes(1 << 30, 1 << 30, 128, 128, 128, ctypes.byref(pb), None) == INVALID
     assert lib.sattn_packed_bytes(1, 1, 1, 1, 128, None, None) == OK
+    # block-count limit 2^22: every launch's work-item count stays below 2^32
+    assert lib.sattn_packed_bytes(1, 1 << 15, 1 << 14, 1 << 14, 128, None, None) == OK
+    assert lib.sattn_packed_bytes(1, (1 << 15) + 1, 1 << 14, 128, 128, None, None) == UNSUPPORTED
+    assert lib.sattn_packed_bytes(2, 1 << 15, 128, 1 << 14, 128, None, None) == UNSUPPORTED
     with pytest.raises(NotImplementedError):
         sattn.packed_bytes(1, 1, 128, 128, 64)
     with pytest.raises(ValueError):
