@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, help="testkit workload index")
-    ap.add_argument("--cpu-rows-per-head", type=int, default=64)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (reference kernel for HBM byte counters)")

@@ -31,8 +31,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "kernels.h"
 #include "layout.h"
 
@@ -99,6 +97,7 @@ __device__ inline void copy_to_lds_off(const uint8_t* src_lane, uint8_t* dst_wav
 // |acc| < 2^22; INT8 MFMA accumulators started from these bits can be read
 // as floats without a conversion.
 constexpr int kMagicBits = 0x4B400000;
+constexpr int kNegInfBits = (int)0xFF800000u;
 constexpr float kMagicF = 12582912.0f;
 
 // ---------------------------------------------------------------------------
@@ -114,7 +113,6 @@ constexpr float kMagicF = 12582912.0f;
 // Tile u lives in LDS stage u % 3 from slot 2u (K read by A) to slot 2u+3
 // (V read by B); group A loads tile t+1 at the start of M(t) and waits for
 // it at the end of V(t).
-template <bool MAGIC, bool PRIO>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int NW = 8;
@@ -161,7 +159,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   // destination base lives in M0, and rewriting M0 waits for the previous
   // LDS-DMA to have consumed it, so M0 is set once per 4 KiB and the
   // instruction's immediate offset (added to both addresses) steps by 1 KiB.
-  auto copy_tile = [&](int t, int stage, int widx, int nwaves) {
+  auto copy_tile = [&](int t, int stage, int widx, int nwaves) __attribute__((always_inline)) {
     const int per = 2048 / nwaves;  // 16-byte pieces per wave
     const int c0 = widx * per;      // first piece, wave-uniform
     const uint8_t* src = (c0 < 1024 ? kbase + (int64_t)t * kTileBytes + c0 * 16
@@ -185,7 +183,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   uint32_t P[2][8];
   v16i S0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) S0[r] = MAGIC ? kMagicBits : 0;
+  for (int r = 0; r < 16; ++r) S0[r] = kMagicBits;
   float c_cur = 0.0f;  // dequant scale of the tile whose S is held
   // The K block scales are read through the constant address space, which
   // makes these uniform loads scalar (s_load, counted by lgkmcnt).  A vector
@@ -195,12 +193,18 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       (const __attribute__((address_space(4))) float*)(ksc);
 
   // ---- M(t): PV of tile t-1, then S of tile t
-  auto mblock = [&](int t, bool do_pv, bool do_s) {
+  // kst = t % 3, the LDS stage of tile t.  The steady-state loop passes it
+  // as a literal, so every LDS address is a lane constant plus an immediate.
+  // mask_rem < 128 (the partial last tile only): keys at or past mask_rem
+  // get the bits of -inf.  As an integer that is below every biased score,
+  // so the row maximum ignores it; as a float it gives exp2(fma(-inf, c, nb))
+  // = 0.  The MFMA-issuing wave waits for these S values here, once per sweep.
+  auto mblock = [&](int t, bool do_pv, bool do_s, int kst, int mask_rem) __attribute__((always_inline)) {
     // the MFMA-issuing wave of the SIMD gets issue priority over its partner
-    if (PRIO) __builtin_amdgcn_s_setprio(2);
-    if (isA && t >= 1 && t + 1 < nbk) copy_tile(t + 1, (t + 1) % 3, w, 4);
+    __builtin_amdgcn_s_setprio(2);
+    if (isA && t >= 1 && t + 1 < nbk) copy_tile(t + 1, kst == 2 ? 0 : kst + 1, w, 4);
     if (do_pv) {
-      const uint8_t* Vs = smem + ((t + 2) % 3) * kStageBytes + kTileBytes;  // stage of t-1
+      const uint8_t* Vs = smem + (kst == 0 ? 2 : kst - 1) * kStageBytes + kTileBytes;  // stage of t-1
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const v8i Bp = {(int)P[g][0], (int)P[g][1], (int)P[g][2], (int)P[g][3],
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     if (do_s) {
-      const uint8_t* Ks = smem + (t % 3) * kStageBytes;
+      const uint8_t* Ks = smem + kst * kStageBytes;
       v4i kf[4][4];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -250,28 +254,37 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       c_cur = qscale * ksc4[t] * p.sl2e;
+      if (mask_rem < 128) {
+        // the first masked key offset of this lane half; the empty asm before
+        // each comparison keeps the 64 lane masks from all being computed up
+        // front and held in SGPRs
+        int rl = mask_rem - 4 * hh;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            asm volatile("" : "+v"(rl));
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rl) S[kb][r] = kNegInfBits;
+          }
+      }
     }
-    if (PRIO) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- V(t): online softmax of S -> P, conditional rescale of O
-  auto vblock = [&](int rem, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    const float c = c_cur;
-    constexpr int kMaskedVal = MAGIC ? 0x4B000000 : -(1 << 30);
-    int mx = kMaskedVal;
+  auto vblock = [&]() __attribute__((always_inline)) {
+    // c = 0 (an all-zero Q or K block: every score of the tile is 0) would
+    // turn masked keys' -inf into NaN; the smallest normal float gives the
+    // same exponent arguments for the valid keys (its products stay far
+    // below their rounding unit) and keeps -inf at -inf.
+    const float c = c_cur == 0.0f ? 1.17549435e-38f : c_cur;
+    int mx = 0x4B000000;  // the bits of 2^23: below every biased score
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kMasked) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= rem) S[kb][r] = kMaskedVal;
-        }
-        mx = max(mx, (int)S[kb][r]);
-      }
+      for (int r = 0; r < 16; ++r) mx = max(mx, (int)S[kb][r]);
     mx = max(mx, other_half_i(mx));
-    const float mt = (MAGIC ? (__int_as_float(mx) - kMagicF) : (float)mx) * c;
+    const float mt = (__int_as_float(mx) - kMagicF) * c;
     const float mnew = fmaxf(m_run, mt);
     if (__any(mnew > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
@@ -282,8 +295,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
     m_run = mnew;
-    const float nb = MAGIC ? __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew) : kLog2_448 - mnew;
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float nb = __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew);
+    float ls[4];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -293,13 +306,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = MAGIC ? __int_as_float(S[kb][r0 + i]) : (float)S[kb][r0 + i];
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, nb));
-          if (kMasked) {
-            const int key = kb * 32 + 8 * (j & 3) + 4 * hh + i;
-            if (key >= rem) pv[i] = 0.0f;
-          }
-          ls[i] += pv[i];
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(S[kb][r0 + i]), c, nb));
+          // the first term starts the sum (p >= 0, so 0 + p == p)
+          ls[i] = (g == 0 && j == 0) ? pv[i] : ls[i] + pv[i];
         }
         // the first conversion writes the low half only: start from the
         // register's old contents instead of materialising a zero
@@ -308,6 +317,14 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         P[g][j] = (uint32_t)wd;
       }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // The results leave the phase here: without these uses the compiler is
+    // free to sink the exponentials past the next barrier into the partner
+    // group's phase, which would undo the MFMA / VALU alternation.
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(P[g][j]));
+    asm volatile("" ::"v"(l_run));
   };
 
   auto barrier = [] { __builtin_amdgcn_s_barrier(); };
@@ -327,21 +344,30 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   if (!isA) barrier();  // group B lags one slot
   const int last = nbk - 1;
   const int rem = p.Nkv - last * 128;
-  int t = 0;
-  for (; t < last; ++t) {
-    mblock(t, t > 0, true);
+  auto step = [&](int t, bool do_pv, int kst) __attribute__((always_inline)) {
+    mblock(t, do_pv, true, kst, 128);
     barrier();
-    vblock(128, std::false_type{});
+    vblock();
     if (isA) wait_loads();
     barrier();
+  };
+  int t = 0;
+  if (last > 0) {
+    step(0, false, 0);
+    t = 1;
   }
-  mblock(last, last > 0, true);
+  for (; t + 3 <= last; t += 3) {
+    step(t, true, 1);
+    step(t + 1, true, 2);
+    step(t + 2, true, 0);
+  }
+  for (; t < last; ++t) step(t, true, t % 3);
+  mblock(last, last > 0, true, last % 3, rem);
   barrier();
-  if (rem >= 128) vblock(rem, std::false_type{});
-  else vblock(rem, std::true_type{});
+  vblock();
   if (isA) wait_loads();
   barrier();
-  mblock(nbk, true, false);
+  mblock(nbk, true, false, nbk % 3, 128);
   if (isA) barrier();
 
   // ---- epilogue: O = acc * vs / l448 -> BF16
@@ -368,17 +394,22 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   }
 }
 
-template <bool MAGIC, bool PRIO>
 hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
   constexpr int BM = 256;
   constexpr int kLds = 3 * kStageBytes;
-  static bool attr_set = false;  // raising the dynamic LDS limit is per function, once
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<MAGIC, PRIO>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  // Raising the dynamic LDS limit is per function and device, once each
+  // (a repeated call from a racing thread is harmless).
+  constexpr int kMaxDev = 64;
+  static bool attr_set[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev || !attr_set[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev >= 0 && dev < kMaxDev) attr_set[dev] = true;
   }
   AttnP p;
   p.q8 = a.packed + L.off_q8;
@@ -400,7 +431,7 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   p.G = L.B * L.H * p.mt;
   p.sl2e = a.softmax_scale * kLog2e;
   const int64_t G8 = (p.G + 7) / 8 * 8;
-  hipLaunchKernelGGL((attn_pp_kernel<MAGIC, PRIO>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
+  hipLaunchKernelGGL(attn_pp_kernel, dim3((unsigned)G8), dim3(512), kLds, stream, p);
   return hipGetLastError();
 }
 
@@ -408,7 +439,7 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
   (void)cross;
-  return launch_pp<true, true>(a, stream);
+  return launch_pp(a, stream);
 }
 
 }  // namespace sattn

@@ -110,6 +110,16 @@ def test_zero_q_matches_closed_form(device):
     check(o, oracle.attention(oracle.quantize(q, k, v), SCALE), v, "Q = 0")
 
 
+def test_zero_k_ragged(device):
+    # every K block scale is 0, so every score is 0; the tail tile is masked
+    log("attention K = 0, ragged")
+    cfg = testkit.CONFIGS[1]
+    q, _, v = testkit.make_inputs(cfg, seed=10, Nq=200, Nkv=333)
+    k = np.zeros((1, 333, 2, 128), np.uint16)
+    o = gpu_attention(q, k, v)
+    check(o, oracle.attention(oracle.quantize(q, k, v), SCALE), v, "K = 0")
+
+
 def test_single_key(device):
     log("attention Nkv = 1")
     cfg = testkit.CONFIGS[1]
