@@ -44,12 +44,12 @@ def _load():
         lib.orc_e4m3_encode_bits.restype = None
         lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
         lib.orc_f32_to_bf16.restype = ctypes.c_uint16
-        lib.orc_quantize.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P, P, P, P]
+        lib.orc_quantize.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_int, P, P, P, P, P, P, P]
         lib.orc_quantize.restype = None
-        lib.orc_attention_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_float,
-                                           I64, P, P, P, P]
+        lib.orc_attention_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
+                                           ctypes.c_float, I64, P, P, P, P]
         lib.orc_attention_rows.restype = None
-        lib.orc_attention.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P]
+        lib.orc_attention.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int, ctypes.c_float, P]
         lib.orc_attention.restype = None
         lib.orc_bruteforce.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
         lib.orc_bruteforce.restype = None
@@ -106,7 +106,13 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
 
 
 # -------------------------------------------------------------- quantize ----
-def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> Dict[str, np.ndarray]:
+QK_FORMATS = {"int8": 0, "fp8": 1}
+
+
+def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray, qk_format: str = "int8") -> Dict[str, np.ndarray]:
+    """Codes and scales; qk_format "int8" (scale amax/127) or "fp8" (E4M3
+    bit patterns, scale amax/448) for Q and smoothed K."""
+    fmt = QK_FORMATS[qk_format]
     B, Nq, H, d = q.shape
     Nkv = k.shape[1]
     assert d == D and k.shape == (B, Nkv, H, D) and v.shape == (B, Nkv, H, D)
@@ -120,9 +126,10 @@ def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> Dict[str, np.ndarra
         "v_scale": np.empty((B, H, D), np.float32),
         "k_mean": np.empty((B, H, D), np.float32),
     }
-    _load().orc_quantize(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nkv,
+    _load().orc_quantize(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nkv, fmt,
                          *(r[n].ctypes.data for n in ("q8", "k8", "v8", "q_scale", "k_scale",
                                                       "v_scale", "k_mean")))
+    r["qk_format"] = qk_format
     return r
 
 
@@ -139,8 +146,8 @@ def attention(codes: Dict[str, np.ndarray], softmax_scale: float) -> np.ndarray:
     Nkv = codes["k8"].shape[2]
     arrs = _code_args(codes)
     out = np.empty((B, Nq, H, D), np.uint16)
-    _load().orc_attention(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv, softmax_scale,
-                          out.ctypes.data)
+    _load().orc_attention(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv,
+                          QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale, out.ctypes.data)
     return out
 
 
@@ -157,7 +164,8 @@ def attention_rows(codes: Dict[str, np.ndarray], softmax_scale: float,
     out = np.empty((n, D), np.uint16)
     m = np.empty(n, np.float64)
     l = np.empty(n, np.float64)
-    _load().orc_attention_rows(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv, softmax_scale, n,
+    _load().orc_attention_rows(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv,
+                               QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale, n,
                                rows.ctypes.data, out.ctypes.data, m.ctypes.data, l.ctypes.data)
     return out, m, l
 

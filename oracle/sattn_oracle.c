@@ -18,6 +18,10 @@
  * amax/127 and round-half-even, per-(batch, head, channel) OCP E4M3 for V with
  * scale amax/448, P scaled by 448 and rounded to E4M3, the row sum taken from
  * FP32 P, and a full two-pass softmax.
+ * A second Q/K format (ORC_QK_FP8) follows the FP8/FP8/BF16 row of the MHA v4
+ * page's MI355X throughput table: Q and mean-smoothed K as OCP E4M3 with
+ * per-block scale amax/448 (the same encoder and clamp as V), and exact
+ * FP64 dot products of the decoded codes.
  *
  * Every loop runs in index order.  FP32 steps are single IEEE operations;
  * this file must be compiled with -ffp-contract=off and without fast-math.
@@ -173,6 +177,25 @@ static int8_t int8_code(float x, float s) {
   return (int8_t)r;
 }
 
+/* E4M3(clamp(x / s, -448, 448)); s == 0 gives 0x00. */
+static uint8_t e4m3_code(float x, float s) {
+  if (s == 0.0f) return 0x00;
+  float y = x / s;             /* one correctly rounded FP32 division */
+  if (y > 448.0f) y = 448.0f;
+  if (y < -448.0f) y = -448.0f;
+  return orc_e4m3_encode(y);
+}
+
+/*
+ * Q/K code formats: ORC_QK_INT8 (scale amax/127, INT8 codes) and
+ * ORC_QK_FP8 (scale amax/448, OCP E4M3 codes stored as their bit patterns).
+ */
+enum { ORC_QK_INT8 = 0, ORC_QK_FP8 = 1 };
+static float qk_max(int fmt) { return fmt == ORC_QK_FP8 ? 448.0f : 127.0f; }
+static int8_t qk_code(float x, float s, int fmt) {
+  return fmt == ORC_QK_FP8 ? (int8_t)e4m3_code(x, s) : int8_code(x, s);
+}
+
 /* ------------------------------------------------------------ quantize ---- */
 
 static int64_t nblocks(int64_t n) { return (n + BLK - 1) / BLK; }
@@ -186,7 +209,7 @@ static int64_t nblocks(int64_t n) { return (n + BLK - 1) / BLK; }
  * outputs: they hold exactly N rows.
  */
 void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt,
                   int8_t* q8, int8_t* k8, uint8_t* v8,
                   float* q_scale, float* k_scale, float* v_scale, float* k_mean) {
   const int64_t nbq = nblocks(Nq), nbk = nblocks(Nkv);
@@ -203,11 +226,11 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
             float x = fabsf(bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]));
             if (x > amax) amax = x;
           }
-        float s = amax / 127.0f;
+        float s = amax / qk_max(fmt);
         q_scale[bh * nbq + t] = s;
         for (int64_t n = n0; n < n1; n++)
           for (int d = 0; d < D; d++)
-            q8[(bh * Nq + n) * D + d] = int8_code(bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]), s);
+            q8[(bh * Nq + n) * D + d] = qk_code(bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]), s, fmt);
       }
       /* --- K mean --- */
       float mean[D];
@@ -231,12 +254,12 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
             float x = fabsf(bf16_to_f32(k[((b * Nkv + n) * H + h) * D + d]) - mean[d]);
             if (x > amax) amax = x;
           }
-        float s = amax / 127.0f;
+        float s = amax / qk_max(fmt);
         k_scale[bh * nbk + t] = s;
         for (int64_t n = n0; n < n1; n++)
           for (int d = 0; d < D; d++) {
             float x = bf16_to_f32(k[((b * Nkv + n) * H + h) * D + d]) - mean[d];
-            k8[(bh * Nkv + n) * D + d] = int8_code(x, s);
+            k8[(bh * Nkv + n) * D + d] = qk_code(x, s, fmt);
           }
       }
       /* --- V --- */
@@ -248,16 +271,8 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         }
         float s = amax / 448.0f;
         v_scale[bh * D + d] = s;
-        for (int64_t n = 0; n < Nkv; n++) {
-          uint8_t c = 0x00;
-          if (s != 0.0f) {
-            float y = bf16_to_f32(v[((b * Nkv + n) * H + h) * D + d]) / s;
-            if (y > 448.0f) y = 448.0f;
-            if (y < -448.0f) y = -448.0f;
-            c = orc_e4m3_encode(y);
-          }
-          v8[(bh * Nkv + n) * D + d] = c;
-        }
+        for (int64_t n = 0; n < Nkv; n++)
+          v8[(bh * Nkv + n) * D + d] = e4m3_code(bf16_to_f32(v[((b * Nkv + n) * H + h) * D + d]), s);
       }
     }
   }
@@ -267,7 +282,9 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /*
  * One output row (b, h, i) from the canonical codes and scales:
- *   acc_j = sum_d q8[i,d] k8[j,d]                       (exact int32)
+ *   acc_j = sum_d q8[i,d] k8[j,d]                       (exact: int32, or
+ *                                                        FP64 of decoded
+ *                                                        E4M3 for FP8 Q/K)
  *   s_j   = acc_j * qs * ks_blk(j) * softmax_scale      (FP64)
  *   m     = max_j s_j                                   (pass 1)
  *   p_j   = (float) exp(s_j - m)                        (pass 2; p in (0,1])
@@ -279,7 +296,7 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  */
 static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                           const float* q_scale, const float* k_scale, const float* v_scale,
-                          int64_t H, int64_t Nq, int64_t Nkv, float softmax_scale,
+                          int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
                           int64_t b, int64_t h, int64_t i,
                           double* sc, float* p, uint16_t* out_row, double* m_out, double* l_out) {
   const int64_t bh = b * H + h;
@@ -289,9 +306,17 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
   double m = -INFINITY;
   for (int64_t j = 0; j < Nkv; j++) {
     const int8_t* kj = k8 + (bh * Nkv + j) * D;
-    int32_t acc = 0;
-    for (int d = 0; d < D; d++) acc += (int32_t)qi[d] * (int32_t)kj[d];
-    double s = (double)acc * qs * (double)k_scale[bh * nbk + j / BLK] * (double)softmax_scale;
+    double acc = 0.0;
+    if (fmt == ORC_QK_FP8) {
+      /* exact in FP64: each product is a multiple of 2^-18 below 2^18 */
+      for (int d = 0; d < D; d++)
+        acc += orc_e4m3_decode((uint8_t)qi[d]) * orc_e4m3_decode((uint8_t)kj[d]);
+    } else {
+      int32_t ia = 0;
+      for (int d = 0; d < D; d++) ia += (int32_t)qi[d] * (int32_t)kj[d];
+      acc = (double)ia;
+    }
+    double s = acc * qs * (double)k_scale[bh * nbk + j / BLK] * (double)softmax_scale;
     sc[j] = s;
     if (s > m) m = s;
   }
@@ -319,7 +344,7 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
 /* Selected rows: rows[3r..3r+2] = (b, h, i).  out: [nrows][128] BF16. */
 void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                         const float* q_scale, const float* k_scale, const float* v_scale,
-                        int64_t B, int64_t H, int64_t Nq, int64_t Nkv, float softmax_scale,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
                         int64_t nrows, const int64_t* rows,
                         uint16_t* out, double* m_out, double* l_out) {
   (void)B;
@@ -329,7 +354,7 @@ void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
     float* p = (float*)malloc(sizeof(float) * (size_t)Nkv);
     #pragma omp for schedule(dynamic)
     for (int64_t r = 0; r < nrows; r++) {
-      attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, softmax_scale,
+      attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
                     rows[3 * r], rows[3 * r + 1], rows[3 * r + 2], sc, p, out + r * D,
                     m_out ? m_out + r : NULL, l_out ? l_out + r : NULL);
     }
@@ -341,7 +366,7 @@ void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
 /* Every row; out is BSHD [B][Nq][H][128] BF16. */
 void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                    const float* q_scale, const float* k_scale, const float* v_scale,
-                   int64_t B, int64_t H, int64_t Nq, int64_t Nkv, float softmax_scale,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
                    uint16_t* out) {
   #pragma omp parallel
   {
@@ -351,7 +376,7 @@ void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
     for (int64_t b = 0; b < B; b++)
       for (int64_t h = 0; h < H; h++)
         for (int64_t i = 0; i < Nq; i++)
-          attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, softmax_scale,
+          attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
                         b, h, i, sc, p, out + ((b * Nq + i) * H + h) * D, NULL, NULL);
     free(sc);
     free(p);
