@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s (4·B·H·Nq·Nkv·D), INT8-QK/FP8-PV, D=128; % of MFMA peak"
+# (with --qk-format fp8 the same figure for the FP8 Q/K format)
 PEAK_TFLOPS = 5000.0     # MI355X dense INT8 / FP8 MFMA
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
 ATTN_KERNEL = "attn_pp_kernel"
@@ -57,19 +58,22 @@ def attn_kernel_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, qk_format):
     """HBM bytes per attention launch from the committed FETCH_SIZE and
     WRITE_SIZE passes, each scaled by what the same counter read for a plain
     device copy of COPY_BYTES; None when there is no record for this workload
     or the kernel sources changed since it was taken."""
     try:
         with open(TRAFFIC_RECORD) as fh:
-            line = next(ln for ln in fh if ln.startswith("traffic-record: "))
-    except (OSError, StopIteration):
+            recs = [json.loads(ln[len("traffic-record: "):]) for ln in fh if ln.startswith("traffic-record: ")]
+    except OSError:
         return None
-    rec = json.loads(line[len("traffic-record: "):])
-    if rec.get("kernel_digest") != attn_kernel_digest() or rec.get("workload") != workload:
+    digest = attn_kernel_digest()
+    recs = [r for r in recs if r.get("kernel_digest") == digest and r.get("workload") == workload
+            and r.get("qk_format", "int8") == qk_format]
+    if not recs:
         return None
+    rec = recs[0]
     fetch = rec["fetch_kib"] * rec["copy_bytes"] / rec["copy_fetch_kib"]
     write = rec["write_kib"] * rec["copy_bytes"] / rec["copy_write_kib"]
     return int(round(fetch + write))
@@ -85,12 +89,12 @@ def copy_calibration(torch, dev):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, q, k, v, rows_per_head):
+def cpu_baseline(cfg, q, k, v, rows_per_head, qk_format):
     import numpy as np
 
     import oracle
     t0 = time.time()
-    codes = oracle.quantize(q, k, v)
+    codes = oracle.quantize(q, k, v, qk_format=qk_format)
     t_quant = time.time() - t0
     stride = max(1, cfg.Nq // rows_per_head)
     rows = np.array([[b, h, i] for b in range(cfg.B) for h in range(cfg.H)
@@ -119,6 +123,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="testkit workload index")
     ap.add_argument("--cpu-rows-per-head", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qk-format", choices=("int8", "fp8"), default="int8",
+                    help="Q/K code format: INT8 (scale amax/127) or E4M3 (scale amax/448)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -145,7 +151,7 @@ def main():
     attend = sattn.fwd if cfg.Nq == cfg.Nkv else sattn.fwd_cross
 
     def step():
-        p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work)
+        p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work, qk_format=args.qk_format)
         ev[1].record()
         attend(p, cfg.softmax_scale, out=out)
         return p
@@ -186,9 +192,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8/fp8",
+        "dtype": "int8/fp8" if args.qk_format == "int8" else "fp8",
         "data": "synthetic",
         "config": dict(cfg.describe(), workload=cfg.name, softmax_scale=cfg.softmax_scale,
+                       qk_format=args.qk_format,
                        step="sattn_quantize_qkv + " + ("sattn_fwd" if cfg.Nq == cfg.Nkv else "sattn_fwd_cross")),
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "attention_only": {"ms": round(t_attn, 4), "ms_min": round(t_attn_min, 4),
@@ -198,14 +205,14 @@ def main():
                      "frac_of_hbm_peak": round(qbytes / (t_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(attn_tf, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(cfg.name),
+                     "traffic": measured_traffic(cfg.name, args.qk_format),
                      "algo_bytes": attn_algo_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv),
                      "kernel_digest": attn_kernel_digest()},
     }
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_rows_per_head)
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_rows_per_head, args.qk_format)
     print(json.dumps(rec), flush=True)
 
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SATTN_ABI_VERSION 1
+#define SATTN_ABI_VERSION 2
 #define SATTN_HEAD_DIM 128
 #define SATTN_BLOCK 128
 /* longest supported sequence (keeps the K mean divisor exact in FP32) */
@@ -72,6 +72,16 @@ typedef enum {
   SATTN_ERR_DEVICE = 4,           /* no HIP device, or the current device is not gfx950 */
   SATTN_ERR_LAUNCH = 5            /* a kernel launch reported an error */
 } sattn_status;
+
+/*
+ * Q/K code formats.  SATTN_QK_INT8: INT8 codes with block scale amax/127
+ * (the INT8/FP8/BF16 path of the gfx1201 backend page, "Changes").
+ * SATTN_QK_FP8: OCP E4M3 codes with block scale amax/448 and an FP8 Q.K^T
+ * MFMA (the FP8/FP8/BF16 row of the MHA v4 page's MI355X throughput table).
+ * V and P are E4M3 in both.  The entry points without a format argument use
+ * SATTN_QK_INT8.
+ */
+typedef enum { SATTN_QK_INT8 = 0, SATTN_QK_FP8 = 1 } sattn_qk_format;
 
 /* ABI version of the loaded library (SATTN_ABI_VERSION). */
 int sattn_abi_version(void);
@@ -127,9 +137,30 @@ sattn_status sattn_fwd_cross(const void* packed, size_t packed_bytes,
                              void* stream);
 
 /*
+ * The same three calls with the Q/K code format as an argument (a format
+ * outside sattn_qk_format is SATTN_ERR_INVALID_ARGUMENT).  The packed layout
+ * and its size are the same for both formats; a packed buffer must be read
+ * with the format it was written with (the library cannot tell them apart).
+ */
+sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
+                                   int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                   const int64_t* q_strides, const int64_t* k_strides,
+                                   const int64_t* v_strides, int qk_format,
+                                   void* packed, size_t packed_bytes,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+sattn_status sattn_fwd_ex(const void* packed, size_t packed_bytes, int qk_format,
+                          int64_t B, int64_t H, int64_t N, int64_t D, float softmax_scale,
+                          void* out, const int64_t* out_strides, void* stream);
+sattn_status sattn_fwd_cross_ex(const void* packed, size_t packed_bytes, int qk_format,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                float softmax_scale, void* out, const int64_t* out_strides,
+                                void* stream);
+
+/*
  * Host-only inspection of a packed buffer (a host copy of it): writes the
  * canonical layouts
- *   q8 [B,H,Nq,128] int8, k8 [B,H,Nkv,128] int8, v8 [B,H,Nkv,128] E4M3 bits,
+ *   q8 [B,H,Nq,128] and k8 [B,H,Nkv,128] (INT8 codes, or E4M3 bits for
+ *   SATTN_QK_FP8), v8 [B,H,Nkv,128] E4M3 bits,
  *   q_scale [B,H,ceil(Nq/128)], k_scale [B,H,ceil(Nkv/128)],
  *   v_scale [B,H,128], k_mean [B,H,128] (FP32).
  * Any output pointer may be NULL to skip it.  No device needed.

@@ -7,10 +7,15 @@ there is no other code path -- if the library is missing or the device is not
 gfx950, calls raise.
 
 Entry points (same names as the C ABI):
-    quantize_qkv(q, k, v)                -> Packed   (preprocessing)
+    quantize_qkv(q, k, v, qk_format)     -> Packed   (preprocessing)
     fwd(packed, softmax_scale, out)      -> Tensor   (self-attention)
     fwd_cross(packed, softmax_scale, out)-> Tensor   (cross-attention)
-    attention(q, k, v, softmax_scale, out)           (both stages)
+    attention(q, k, v, softmax_scale, out, qk_format=...)  (both stages)
+
+``qk_format`` is "int8" (INT8 Q/K codes, scale amax/127: the gfx1201 backend
+page's INT8/FP8/BF16 path) or "fp8" (E4M3 Q/K codes, scale amax/448: the
+FP8/FP8/BF16 row of the MHA v4 page's MI355X table).  A Packed buffer records
+its format and the forward calls pass it on (the ``_ex`` C entry points).
 
 As the gfx1201 backend page specifies its backend ("[ROCm] Add
 aiter_sage_attn attention backend for gfx1201 (RDNA4)", Changes): BF16
@@ -29,7 +34,7 @@ from typing import Dict, Optional, Tuple
 
 import torch
 
-__all__ = ["Packed", "SattnError", "abi_version", "packed_bytes", "quantize_qkv", "fwd",
+__all__ = ["Packed", "SattnError", "QK_FORMATS", "abi_version", "packed_bytes", "quantize_qkv", "fwd",
            "fwd_cross", "attention", "unpack_host", "e4m3_encode", "library_path"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +48,7 @@ SATTN_ERR_BUFFER_TOO_SMALL = 3
 SATTN_ERR_DEVICE = 4
 SATTN_ERR_LAUNCH = 5
 HEAD_DIM = 128
+QK_FORMATS = {"int8": 0, "fp8": 1}  # sattn_qk_format
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -72,9 +78,15 @@ def _load():
         lib.sattn_quantize_qkv.argtypes = [_P, _P, _P] + [_I64] * 5 + [_I64P] * 3 + [_P, _SZ, _P, _SZ, _P]
         lib.sattn_fwd.argtypes = [_P, _SZ] + [_I64] * 4 + [ctypes.c_float, _P, _I64P, _P]
         lib.sattn_fwd_cross.argtypes = [_P, _SZ] + [_I64] * 5 + [ctypes.c_float, _P, _I64P, _P]
+        lib.sattn_quantize_qkv_ex.argtypes = ([_P, _P, _P] + [_I64] * 5 + [_I64P] * 3 + [ctypes.c_int]
+                                              + [_P, _SZ, _P, _SZ, _P])
+        lib.sattn_fwd_ex.argtypes = [_P, _SZ, ctypes.c_int] + [_I64] * 4 + [ctypes.c_float, _P, _I64P, _P]
+        lib.sattn_fwd_cross_ex.argtypes = ([_P, _SZ, ctypes.c_int] + [_I64] * 5
+                                           + [ctypes.c_float, _P, _I64P, _P])
         lib.sattn_unpack_host.argtypes = [_P, _SZ] + [_I64] * 5 + [_P] * 7
         lib.sattn_e4m3_encode.argtypes = [_P, _P, _I64, _P]
         for f in ("sattn_packed_bytes", "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_cross",
+                  "sattn_quantize_qkv_ex", "sattn_fwd_ex", "sattn_fwd_cross_ex",
                   "sattn_unpack_host", "sattn_e4m3_encode"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -113,6 +125,7 @@ class Packed:
     Nq: int
     Nkv: int
     squeeze_batch: bool = False
+    qk_format: str = "int8"
 
 
 def _stream_ptr(device: torch.device) -> int:
@@ -141,10 +154,18 @@ def _strides(x: torch.Tensor):
     return (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
 
 
+def _format(qk_format: str) -> int:
+    if qk_format not in QK_FORMATS:
+        raise ValueError(f"qk_format must be one of {sorted(QK_FORMATS)}, got {qk_format!r}")
+    return QK_FORMATS[qk_format]
+
+
 def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  packed: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Packed:
-    """BF16 q [B,Nq,H,128], k/v [B,Nkv,H,128] -> packed INT8/E4M3 codes and scales."""
+                 workspace: Optional[torch.Tensor] = None, qk_format: str = "int8") -> Packed:
+    """BF16 q [B,Nq,H,128], k/v [B,Nkv,H,128] -> packed Q/K codes (INT8 or
+    E4M3, per ``qk_format``), E4M3 V codes and scales."""
+    fmt = _format(qk_format)
     q4, sq = _as4d(q, "q")
     k4, _ = _as4d(k, "k")
     v4, _ = _as4d(v, "v")
@@ -160,11 +181,12 @@ def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(wb, dtype=torch.uint8, device=q4.device)
     qs, ks, vs = _strides(q4), _strides(k4), _strides(v4)
-    _check(_load().sattn_quantize_qkv(q4.data_ptr(), k4.data_ptr(), v4.data_ptr(), B, H, Nq, Nkv, D,
-                                      qs, ks, vs, packed.data_ptr(), packed.numel() * packed.element_size(),
-                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                      _stream_ptr(q4.device)), "sattn_quantize_qkv")
-    return Packed(packed, B, H, Nq, Nkv, sq)
+    _check(_load().sattn_quantize_qkv_ex(q4.data_ptr(), k4.data_ptr(), v4.data_ptr(), B, H, Nq, Nkv, D,
+                                         qs, ks, vs, fmt, packed.data_ptr(),
+                                         packed.numel() * packed.element_size(), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_ptr(q4.device)), "sattn_quantize_qkv")
+    return Packed(packed, B, H, Nq, Nkv, sq, qk_format)
 
 
 def _scale(softmax_scale: Optional[float]) -> float:
@@ -187,9 +209,9 @@ def fwd(packed: Packed, softmax_scale: Optional[float] = None,
     res, o4 = _out(packed, out)
     if packed.Nq != packed.Nkv:
         raise NotImplementedError("fwd needs Nq == Nkv; use fwd_cross")
-    _check(_load().sattn_fwd(packed.buf.data_ptr(), packed.buf.numel(), packed.B, packed.H, packed.Nq,
-                             HEAD_DIM, _scale(softmax_scale), o4.data_ptr(), _strides(o4),
-                             _stream_ptr(o4.device)), "sattn_fwd")
+    _check(_load().sattn_fwd_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+                                packed.B, packed.H, packed.Nq, HEAD_DIM, _scale(softmax_scale),
+                                o4.data_ptr(), _strides(o4), _stream_ptr(o4.device)), "sattn_fwd")
     return res
 
 
@@ -197,17 +219,18 @@ def fwd_cross(packed: Packed, softmax_scale: Optional[float] = None,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Cross-attention (any Nq, Nkv) from a packed buffer; BF16 output."""
     res, o4 = _out(packed, out)
-    _check(_load().sattn_fwd_cross(packed.buf.data_ptr(), packed.buf.numel(), packed.B, packed.H,
-                                   packed.Nq, packed.Nkv, HEAD_DIM, _scale(softmax_scale),
-                                   o4.data_ptr(), _strides(o4), _stream_ptr(o4.device)),
-           "sattn_fwd_cross")
+    _check(_load().sattn_fwd_cross_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+                                      packed.B, packed.H, packed.Nq, packed.Nkv, HEAD_DIM,
+                                      _scale(softmax_scale), o4.data_ptr(), _strides(o4),
+                                      _stream_ptr(o4.device)), "sattn_fwd_cross")
     return res
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
               causal: bool = False, attn_mask: Optional[torch.Tensor] = None,
-              dropout_p: float = 0.0, cu_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
+              dropout_p: float = 0.0, cu_seqlens: Optional[torch.Tensor] = None,
+              qk_format: str = "int8") -> torch.Tensor:
     """Quantize and attend.  Rejects what this path does not compute."""
     if causal:
         raise NotImplementedError("causal attention is not supported")
@@ -217,7 +240,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise NotImplementedError("dropout is not supported")
     if cu_seqlens is not None:
         raise NotImplementedError("packed multi-sequence (cu_seqlens) inputs are not supported")
-    p = quantize_qkv(q, k, v)
+    p = quantize_qkv(q, k, v, qk_format=qk_format)
     if p.Nq == p.Nkv:
         return fwd(p, softmax_scale, out)
     return fwd_cross(p, softmax_scale, out)
@@ -242,6 +265,7 @@ def unpack_host(packed: Packed) -> Dict[str, "object"]:
                                      *(r[n].ctypes.data for n in ("q8", "k8", "v8", "q_scale",
                                                                   "k_scale", "v_scale", "k_mean"))),
            "sattn_unpack_host")
+    r["qk_format"] = packed.qk_format
     return r
 
 

@@ -80,11 +80,14 @@ sattn_status check_device() {
 
 sattn_status launch_status(hipError_t e) { return e == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH; }
 
-sattn_status fwd_common(const void* packed, size_t packed_bytes, int64_t B, int64_t H, int64_t Nq,
-                        int64_t Nkv, int64_t D, float softmax_scale, void* out,
+bool valid_format(int f) { return f == SATTN_QK_INT8 || f == SATTN_QK_FP8; }
+
+sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, int64_t B, int64_t H,
+                        int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale, void* out,
                         const int64_t* out_strides, void* stream, bool cross) {
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
+  if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
   if (packed == nullptr || out == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(packed) || !aligned16(out)) return SATTN_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return SATTN_ERR_INVALID_ARGUMENT;
@@ -98,6 +101,7 @@ sattn_status fwd_common(const void* packed, size_t packed_bytes, int64_t B, int6
   a.packed = static_cast<const uint8_t*>(packed);
   a.softmax_scale = softmax_scale;
   a.out = static_cast<uint16_t*>(out);
+  a.fp8qk = qk_format == SATTN_QK_FP8;
   return launch_status(sattn::launch_attention(a, cross, static_cast<hipStream_t>(stream)));
 }
 
@@ -129,14 +133,15 @@ sattn_status sattn_packed_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, i
   return SATTN_OK;
 }
 
-sattn_status sattn_quantize_qkv(const void* q, const void* k, const void* v,
-                                int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
-                                const int64_t* q_strides, const int64_t* k_strides,
-                                const int64_t* v_strides,
-                                void* packed, size_t packed_bytes,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
+                                   int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                   const int64_t* q_strides, const int64_t* k_strides,
+                                   const int64_t* v_strides, int qk_format,
+                                   void* packed, size_t packed_bytes,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
+  if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !packed || !workspace) return SATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(packed) || !aligned16(workspace))
     return SATTN_ERR_INVALID_ARGUMENT;
@@ -154,21 +159,47 @@ sattn_status sattn_quantize_qkv(const void* q, const void* k, const void* v,
   a.v = static_cast<const uint16_t*>(v);
   a.packed = static_cast<uint8_t*>(packed);
   a.workspace = static_cast<uint8_t*>(workspace);
+  a.fp8qk = qk_format == SATTN_QK_FP8;
   return launch_status(sattn::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+sattn_status sattn_quantize_qkv(const void* q, const void* k, const void* v,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                const int64_t* q_strides, const int64_t* k_strides,
+                                const int64_t* v_strides,
+                                void* packed, size_t packed_bytes,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return sattn_quantize_qkv_ex(q, k, v, B, H, Nq, Nkv, D, q_strides, k_strides, v_strides,
+                               SATTN_QK_INT8, packed, packed_bytes, workspace, workspace_bytes,
+                               stream);
+}
+
+sattn_status sattn_fwd_ex(const void* packed, size_t packed_bytes, int qk_format, int64_t B,
+                          int64_t H, int64_t N, int64_t D, float softmax_scale, void* out,
+                          const int64_t* out_strides, void* stream) {
+  return fwd_common(packed, packed_bytes, qk_format, B, H, N, N, D, softmax_scale, out, out_strides,
+                    stream, false);
+}
+
+sattn_status sattn_fwd_cross_ex(const void* packed, size_t packed_bytes, int qk_format, int64_t B,
+                                int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale,
+                                void* out, const int64_t* out_strides, void* stream) {
+  return fwd_common(packed, packed_bytes, qk_format, B, H, Nq, Nkv, D, softmax_scale, out,
+                    out_strides, stream, true);
 }
 
 sattn_status sattn_fwd(const void* packed, size_t packed_bytes, int64_t B, int64_t H, int64_t N,
                        int64_t D, float softmax_scale, void* out, const int64_t* out_strides,
                        void* stream) {
-  return fwd_common(packed, packed_bytes, B, H, N, N, D, softmax_scale, out, out_strides, stream,
-                    false);
+  return sattn_fwd_ex(packed, packed_bytes, SATTN_QK_INT8, B, H, N, D, softmax_scale, out,
+                      out_strides, stream);
 }
 
 sattn_status sattn_fwd_cross(const void* packed, size_t packed_bytes, int64_t B, int64_t H,
                              int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale, void* out,
                              const int64_t* out_strides, void* stream) {
-  return fwd_common(packed, packed_bytes, B, H, Nq, Nkv, D, softmax_scale, out, out_strides,
-                    stream, true);
+  return sattn_fwd_cross_ex(packed, packed_bytes, SATTN_QK_INT8, B, H, Nq, Nkv, D, softmax_scale,
+                            out, out_strides, stream);
 }
 
 sattn_status sattn_unpack_host(const void* packed_host, size_t packed_bytes, int64_t B, int64_t H,

@@ -113,6 +113,10 @@ constexpr float kMagicF = 12582912.0f;
 // Tile u lives in LDS stage u % 3 from slot 2u (K read by A) to slot 2u+3
 // (V read by B); group A loads tile t+1 at the start of M(t) and waits for
 // it at the end of V(t).
+// FP8QK: Q and K codes are E4M3 (the FP8/FP8/BF16 format): S^T comes from
+// v_mfma_scale_f32_32x32x64_f8f6f4 in FP32, the K operands being the same
+// LDS reads taken two 16-byte chunks per MFMA.
+template <bool FP8QK>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int NW = 8;
@@ -240,19 +244,42 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         }
       // m-outer: the four accumulation chains (one per key block) interleave,
       // so no MFMA waits on the result of the one just issued
+      if constexpr (FP8QK) {
+        // channels 64 hh + 32 c + [0, 32) feed the MFMA of half c
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], S0, 0, 0, 0);
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int m = 1; m < 4; ++m)
+          for (int kb = 0; kb < 4; ++kb) {
+            const v4i a0 = kf[kb][2 * c], a1 = kf[kb][2 * c + 1];
+            const v4i b0 = qf[2 * c], b1 = qf[2 * c + 1];
+            const v8i A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const v8i Bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            const v16f acc = c == 0 ? v16f{} : __builtin_bit_cast(v16f, S[kb]);
+            S[kb] = __builtin_bit_cast(
+                v16i, __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, Bq, acc, 0, 0, 0, 127, 0, 127));
+          }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][m], qf[m], S[kb], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], S0, 0, 0, 0);
+#pragma unroll
+        for (int m = 1; m < 4; ++m)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][m], qf[m], S[kb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       c_cur = qscale * ksc4[t] * p.sl2e;
       if (mask_rem < 128) {
         // the first masked key offset of this lane half; the empty asm before
@@ -278,13 +305,25 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     // same exponent arguments for the valid keys (its products stay far
     // below their rounding unit) and keeps -inf at -inf.
     const float c = c_cur == 0.0f ? 1.17549435e-38f : c_cur;
-    int mx = 0x4B000000;  // the bits of 2^23: below every biased score
+    float mt;
+    if constexpr (FP8QK) {
+      // FP32 scores (unscaled); masked keys are -inf
+      float mx = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = max(mx, (int)S[kb][r]);
-    mx = max(mx, other_half_i(mx));
-    const float mt = (__int_as_float(mx) - kMagicF) * c;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, __int_as_float(S[kb][r]));
+      mx = fmaxf(mx, other_half_f(mx));
+      mt = mx * c;
+    } else {
+      int mx = 0x4B000000;  // the bits of 2^23: below every biased score
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = max(mx, (int)S[kb][r]);
+      mx = max(mx, other_half_i(mx));
+      mt = (__int_as_float(mx) - kMagicF) * c;
+    }
     const float mnew = fmaxf(m_run, mt);
     if (__any(mnew > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
@@ -295,7 +334,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
     m_run = mnew;
-    const float nb = __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew);
+    // exponent argument fma(S_f, c, nb) = (score - m) log2 e + log2 448; for
+    // INT8 codes the float view of S carries the bias 1.5 * 2^23
+    const float nb = FP8QK ? kLog2_448 - mnew : __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew);
     float ls[4];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -394,6 +435,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   }
 }
 
+template <bool FP8QK>
 hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
   constexpr int BM = 256;
@@ -406,7 +448,7 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDev || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<FP8QK>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDev) attr_set[dev] = true;
@@ -431,7 +473,7 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   p.G = L.B * L.H * p.mt;
   p.sl2e = a.softmax_scale * kLog2e;
   const int64_t G8 = (p.G + 7) / 8 * 8;
-  hipLaunchKernelGGL(attn_pp_kernel, dim3((unsigned)G8), dim3(512), kLds, stream, p);
+  hipLaunchKernelGGL(attn_pp_kernel<FP8QK>, dim3((unsigned)G8), dim3(512), kLds, stream, p);
   return hipGetLastError();
 }
 
@@ -439,7 +481,7 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
   (void)cross;
-  return launch_pp(a, stream);
+  return a.fp8qk ? launch_pp<true>(a, stream) : launch_pp<false>(a, stream);
 }
 
 }  // namespace sattn

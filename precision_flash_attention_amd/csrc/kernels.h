@@ -15,6 +15,7 @@ struct QuantArgs {
   Layout L;
   uint8_t* packed;
   uint8_t* workspace;
+  bool fp8qk;  // Q/K as E4M3 with block scale amax/448 instead of INT8 (amax/127)
 };
 
 struct AttnArgs {
@@ -23,6 +24,7 @@ struct AttnArgs {
   float softmax_scale;
   uint16_t* out;
   int64_t o_str[3];
+  bool fp8qk;  // the packed Q/K codes are E4M3
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);

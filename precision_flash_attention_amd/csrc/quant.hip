@@ -9,8 +9,10 @@
 //   2. finalize: per (b, h, channel) the K mean (block sums added in block
 //                order, one division by Nkv) and the V scale amax/448.
 //   3. codes:    per (b, h, block) Q and mean-smoothed K to INT8 with scale
-//                amax/127 and round-half-even; V to E4M3 with its channel
-//                scale, written transposed in the attention kernel's order.
+//                amax/127 and round-half-even (or, in the FP8 Q/K format of
+//                the MHA v4 page's FP8/FP8/BF16 row, to E4M3 with scale
+//                amax/448); V to E4M3 with its channel scale, written
+//                transposed in the attention kernel's order.
 //
 // The codes must equal those of the plain definition bit for bit, where the
 // quotient x / s is one correctly rounded FP32 division.  A full division
@@ -216,6 +218,7 @@ struct CodeP {
   const uint16_t* v;
   int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2;
   int64_t H, Nq, Nkv, nbq, nbk, BH;
+  int fp8qk;
   uint8_t* q8;
   uint8_t* k8;
   uint8_t* v8;
@@ -309,7 +312,8 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
     return;
   }
 
-  // ---- Q and K: block amax, scale amax/127, INT8 codes.
+  // ---- Q and K: block amax, scale amax/127 with INT8 codes, or amax/448
+  // with E4M3 codes (the FP8 Q/K format).
   if (kind == 1) {
     float mean[8];
 #pragma unroll
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
   if ((tid & 63) == 0) red[tid >> 6] = am;
   __syncthreads();
   am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = __fdiv_rn(am, 127.0f);
+  const float s = __fdiv_rn(am, p.fp8qk ? 448.0f : 127.0f);
   const bool ex = s < kFltMin;
   const float r = ex ? 0.0f : __fdiv_rn(1.0f, s);
   if (tid == 0) (kind == 0 ? p.q_scale : p.k_scale)[bh * (kind == 0 ? p.nbq : p.nbk) + t] = s;
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
     if (valid[i] && s != 0.0f) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const uint32_t code = (uint32_t)(int8_code(x[i][c], s, r, ex) & 0xFF);
+        const uint32_t code = p.fp8qk ? e4m3_code(x[i][c], s, r, ex) : (uint32_t)(int8_code(x[i][c], s, r, ex) & 0xFF);
         w[c >> 2] |= code << (8 * (c & 3));
       }
     }
@@ -382,7 +386,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   CodeP cp{a.q, a.k, a.v,
            a.q_str[0], a.q_str[1], a.q_str[2], a.k_str[0], a.k_str[1], a.k_str[2],
            a.v_str[0], a.v_str[1], a.v_str[2],
-           L.H, L.Nq, L.Nkv, L.nbq, L.nbk, BH,
+           L.H, L.Nq, L.Nkv, L.nbq, L.nbk, BH, a.fp8qk ? 1 : 0,
            a.packed + L.off_q8, a.packed + L.off_k8, a.packed + L.off_v8,
            q_scale, k_scale, v_scale, k_mean};
   hipLaunchKernelGGL(k_codes, dim3((unsigned)(BH * (L.nbq + 2 * L.nbk))), dim3(256), 0, stream, cp);

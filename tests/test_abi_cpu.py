@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert sattn.abi_version() == 1
+    assert sattn.abi_version() == 2
     for s in range(6):
         assert lib.sattn_status_string(s)
     assert lib.sattn_status_string(99) == b"unknown status"
@@ -133,6 +133,27 @@ def test_forward_validation(lib, cross):
     assert fwd_call(lib, cross, pbytes=1000) == SMALL
     assert fwd_call(lib, cross, os=strides(1 << 20, 100, 128)) == INVALID
     assert fwd_call(lib, cross) == DEVICE
+
+
+def test_format_entry_points_validation(lib):
+    """The _ex calls take the Q/K code format (0 = INT8, 1 = FP8); any other
+    value is an invalid argument, checked before the device."""
+    q = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED)
+    st = strides(65536, 256, 128)
+    for fmt, want in ((0, DEVICE), (1, DEVICE), (2, INVALID), (-1, INVALID)):
+        assert lib.sattn_quantize_qkv_ex(q["q"], q["k"], q["v"], 1, 2, 256, 256, 128, st, None, None, fmt,
+                                         ALIGNED, 1 << 40, ALIGNED, 1 << 40, None) == want, fmt
+        assert lib.sattn_fwd_ex(ALIGNED, 1 << 40, fmt, 1, 2, 256, 128, ctypes.c_float(0.088), ALIGNED,
+                                None, None) == want, fmt
+        assert lib.sattn_fwd_cross_ex(ALIGNED, 1 << 40, fmt, 1, 2, 256, 300, 128, ctypes.c_float(0.088),
+                                      ALIGNED, None, None) == want, fmt
+    # the shape checks come first, as in the calls without a format
+    assert lib.sattn_fwd_ex(ALIGNED, 1 << 40, 1, 1, 2, 256, 64, ctypes.c_float(0.088), ALIGNED,
+                            None, None) == UNSUPPORTED
+    assert lib.sattn_quantize_qkv_ex(q["q"], q["k"], q["v"], 1, 2, 256, 256, 128, st, None, None, 1,
+                                     ALIGNED, 100, ALIGNED, 1 << 40, None) == SMALL
+    with pytest.raises(ValueError):
+        sattn._format("int4")
 
 
 def test_e4m3_validation(lib):

@@ -1,0 +1,205 @@
+"""GPU parity of the FP8 Q/K format (the FP8/FP8/BF16 row of the MHA v4
+page's MI355X throughput table): Q and mean-smoothed K as OCP E4M3 codes with
+block scale amax/448, an FP8 Q.K^T MFMA, the rest of the method unchanged.
+
+Codes and scales are bit-exact against ``oracle.quantize(..., qk_format="fp8")``.
+Outputs are compared with the FP8 oracle, whose scores are the exact dot
+products of the decoded codes, at cosine >= 0.9995 and
+
+    max |O_gpu - O_oracle| <= (2e-2 + 2 * delta) * max|V|,
+
+where 2e-2 is the bar of the INT8 format and delta bounds the score error of
+the FP8 matrix instruction.  On gfx950, v_mfma_scale_f32_32x32x64_f8f6f4 does
+not return the correctly rounded FP32 sum of its 64 products: measured on
+random and on attention codes, its error reaches 2.7e-4 (about 2^-11.9) of the
+sum of the products' magnitudes, and only about 5% of the results equal the
+rounded exact sum (the INT8 instruction is exact).  A score error of at most
+delta (natural-log units) moves each softmax output by at most 2 * delta *
+max|V| to first order, so the bar takes delta = 2^-11 * max_ij sum_d
+|q_id k_jd| * qs * ks * softmax_scale over the compared rows, from the
+oracle's codes.  That bound is loose (2 to 4 times the largest error seen),
+so the small cases (up to 2^24 query-key pairs) also check that the kernel
+stays as close to exact FP64 attention of the BF16 inputs as the oracle does:
+the E4M3 rounding of Q and K (relative step 2^-4) outweighs the
+instruction's 2^-12."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import precision_flash_attention_amd as sattn
+import testkit
+from gpu_helpers import (MAX_ERR, MIN_COS, assert_codes_equal, from_dev, log, parity, sample_rows,
+                         to_dev, workload)
+
+pytestmark = pytest.mark.gpu
+SCALE = 1.0 / math.sqrt(128.0)
+FMT = "fp8"
+
+
+def gpu_run(q, k, v, scale=SCALE):
+    p = sattn.quantize_qkv(to_dev(q), to_dev(k), to_dev(v), qk_format=FMT)
+    assert p.qk_format == FMT
+    o = sattn.fwd(p, scale) if p.Nq == p.Nkv else sattn.fwd_cross(p, scale)
+    return from_dev(o), sattn.unpack_host(p)
+
+
+def maxv(v):
+    return float(np.abs(testkit.bf16_to_f32(v)).max())
+
+
+HW_DOT_REL = 2.0 ** -11  # FP8 MFMA dot error / sum |products|, measured <= 2^-11.9
+
+
+def score_error_bound(codes, scale, rows=None):
+    """delta: a bound on |score_gpu - score_exact| (natural-log units) over the
+    query rows compared (all rows, or rows[:, (b, h, i)])."""
+    B, H, Nq, _ = codes["q8"].shape
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            if rows is None:
+                qi = np.arange(Nq)
+            else:
+                qi = rows[(rows[:, 0] == b) & (rows[:, 1] == h), 2]
+                if qi.size == 0:
+                    continue
+            qa = np.abs(oracle.e4m3_decode(codes["q8"][b, h, qi].view(np.uint8)))
+            ka = np.abs(oracle.e4m3_decode(codes["k8"][b, h].view(np.uint8)))
+            qs = codes["q_scale"][b, h][qi // 128].astype(np.float64)
+            ks = codes["k_scale"][b, h][np.arange(ka.shape[0]) // 128].astype(np.float64)
+            mag = (qa * qs[:, None]) @ (ka * ks[:, None]).T   # sum_d |q_id k_jd| qs ks
+            worst = max(worst, float(mag.max()))
+    return HW_DOT_REL * worst * scale
+
+
+def check(o_gpu, o_orc, v, what, delta):
+    err, c = parity(o_gpu, o_orc, maxv(v))
+    bar = MAX_ERR + 2.0 * delta
+    log(f"  {what}: max err / max|V| = {err:.3e} (bar {bar:.3e}, delta {delta:.2e}), cos = {c:.7f}")
+    assert err <= bar and c >= MIN_COS, (err, bar, c)
+
+
+def cos(a, b):
+    return float(a @ b / np.sqrt((a @ a) * (b @ b)))
+
+
+def check_case(q, k, v, what, scale=SCALE):
+    o, got = gpu_run(q, k, v, scale)
+    want = oracle.quantize(q, k, v, qk_format=FMT)
+    assert_codes_equal(got, want)
+    ref = oracle.attention(want, scale)
+    check(o, ref, v, what, score_error_bound(want, scale))
+    if q.shape[0] * q.shape[1] * q.shape[2] * k.shape[1] > 1 << 24:
+        return  # exact FP64 attention only where it takes a moment
+    exact = oracle.bruteforce(q, k, v, scale).ravel()
+    c_gpu = cos(testkit.bf16_to_f32(o).astype(np.float64).ravel(), exact)
+    c_orc = cos(testkit.bf16_to_f32(ref).astype(np.float64).ravel(), exact)
+    log(f"    vs exact attention: kernel cos {c_gpu:.6f}, oracle cos {c_orc:.6f}")
+    assert c_gpu >= c_orc - 2e-4
+
+
+@pytest.mark.parametrize("cfg_index", [1, 2])
+def test_full_size_codes_and_full_output(device, cfg_index):
+    log(f"fp8 Q/K parity (codes + full output), workload {cfg_index}")
+    cfg, q, k, v, _ = workload(cfg_index)
+    check_case(q, k, v, cfg.name)
+
+
+@pytest.mark.parametrize("cfg_index", [3, 4, 5])
+def test_full_size_codes_and_sampled_rows(device, cfg_index):
+    log(f"fp8 Q/K parity (codes + sampled rows), workload {cfg_index}")
+    cfg, q, k, v, _ = workload(cfg_index)
+    o, got = gpu_run(q, k, v)
+    want = oracle.quantize(q, k, v, qk_format=FMT)
+    assert_codes_equal(got, want)
+    assert not np.any(np.isnan(testkit.bf16_to_f32(o)))
+    rows = sample_rows(cfg.B, cfg.H, cfg.Nq, 12, seed=50 + cfg_index)
+    ref, _, _ = oracle.attention_rows(want, SCALE, rows)
+    check(o[rows[:, 0], rows[:, 2], rows[:, 1]], ref, v, f"{cfg.name}, {len(rows)} rows",
+          score_error_bound(want, SCALE, rows))
+
+
+@pytest.mark.parametrize("N", [1, 2, 127, 129, 257, 600])
+def test_ragged_self(device, N):
+    log(f"fp8 Q/K tails N={N}")
+    cfg = testkit.CONFIGS[4]
+    q, k, v = testkit.make_inputs(cfg, seed=300 + N, H=3, Nq=N, Nkv=N)
+    check_case(q, k, v, f"N={N}")
+
+
+@pytest.mark.parametrize("Nq,Nkv", [(300, 512), (1, 1000), (129, 1), (1000, 130)])
+def test_cross_shapes(device, Nq, Nkv):
+    log(f"fp8 Q/K cross Nq={Nq} Nkv={Nkv}")
+    cfg = testkit.CONFIGS[3]
+    q, k, v = testkit.make_inputs(cfg, seed=12, B=2, H=3, Nq=Nq, Nkv=Nkv)
+    check_case(q, k, v, f"{Nq}x{Nkv}")
+
+
+@pytest.mark.parametrize("scale", [0.01, 0.2])
+def test_softmax_scales(device, scale):
+    log(f"fp8 Q/K softmax_scale={scale}")
+    cfg = testkit.CONFIGS[2]
+    q, k, v = testkit.make_inputs(cfg, seed=5, H=2, Nq=512, Nkv=512)
+    check_case(q, k, v, f"scale {scale}", scale)
+
+
+def _bf16(x):
+    f = np.asarray(x, np.float32)
+    u = f.view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_zero_and_subnormal_blocks(device):
+    # Q block 1 all zero (scale 0, codes 0); Q block 2 and K of head 1 with
+    # BF16-subnormal values (subnormal FP32 scale amax/448: the exact
+    # division path); a zero K head (every score 0) with a ragged tail
+    log("fp8 Q/K zero and subnormal blocks")
+    rng = np.random.default_rng(8)
+    N, H = 333, 3
+    q = rng.normal(size=(1, N, H, 128)).astype(np.float32)
+    k = rng.normal(size=(1, N, H, 128)).astype(np.float32)
+    v = rng.normal(size=(1, N, H, 128)).astype(np.float32)
+    q[0, 128:256] = 0.0
+    q[0, 256:, 0] = rng.integers(-100, 100, size=(N - 256, 128)) * 2.0 ** -133
+    k[0, :, 1] = rng.integers(-100, 100, size=(N, 128)) * 2.0 ** -133
+    k[0, :, 2] = 0.0
+    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    want = oracle.quantize(q, k, v, qk_format=FMT)
+    assert np.all(want["q_scale"][0, :, 1] == 0.0)
+    assert 0.0 < want["q_scale"][0, 0, 2] < np.finfo(np.float32).tiny
+    check_case(q, k, v, "zero / subnormal blocks")
+
+
+def test_zero_q_matches_closed_form(device):
+    log("fp8 Q/K attention Q = 0")
+    cfg = testkit.CONFIGS[1]
+    _, k, v = testkit.make_inputs(cfg, seed=9, Nq=130, Nkv=300)
+    q = np.zeros((1, 130, 2, 128), np.uint16)
+    check_case(q, k, v, "Q = 0")
+
+
+def test_formats_share_v_codes_and_differ_in_qk(device):
+    # the packed layout is the same for both formats; V codes, V scales and
+    # the K mean do not depend on the Q/K format
+    cfg = testkit.CONFIGS[2]
+    q, k, v = testkit.make_inputs(cfg, seed=3, H=2, Nq=256, Nkv=384)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    a = sattn.unpack_host(sattn.quantize_qkv(qd, kd, vd, qk_format="int8"))
+    b = sattn.unpack_host(sattn.quantize_qkv(qd, kd, vd, qk_format="fp8"))
+    for n in ("v8", "v_scale", "k_mean"):
+        assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), n
+    assert np.array_equal(a["q_scale"] * np.float32(127.0) > 0, b["q_scale"] * np.float32(448.0) > 0)
+    assert not np.array_equal(a["q8"], b["q8"])
+
+
+def test_invalid_format_raises(device):
+    import torch
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ValueError):
+        sattn.quantize_qkv(q, q, q, qk_format="e5m2")
+    p = sattn.quantize_qkv(q, q, q, qk_format="fp8")
+    p.qk_format = "int4"
+    with pytest.raises(ValueError):
+        sattn.fwd(p)

@@ -12,8 +12,8 @@ from gpu_helpers import assert_codes_equal, log, to_dev, workload
 pytestmark = pytest.mark.gpu
 
 
-def gpu_codes(q, k, v):
-    p = sattn.quantize_qkv(to_dev(q), to_dev(k), to_dev(v))
+def gpu_codes(q, k, v, qk_format="int8"):
+    p = sattn.quantize_qkv(to_dev(q), to_dev(k), to_dev(v), qk_format=qk_format)
     return sattn.unpack_host(p)
 
 
@@ -66,8 +66,9 @@ def _bf16(x):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def test_adversarial_blocks(device):
-    log("quantize adversarial blocks")
+@pytest.mark.parametrize("qk_format", ["int8", "fp8"])
+def test_adversarial_blocks(device, qk_format):
+    log(f"quantize adversarial blocks ({qk_format} Q/K)")
     rng = np.random.default_rng(5)
     N, H = 512, 4
     q = np.zeros((1, N, H, 128), np.float32)
@@ -96,7 +97,7 @@ def test_adversarial_blocks(device):
     k[0, :, 1] = rng.normal(size=(N, 128)) * 2.0 ** -125
     q[0, :, 1:] = rng.normal(size=(N, H - 1, 128))
     qb, kb, vb = _bf16(q), _bf16(k), _bf16(v)
-    assert_codes_equal(gpu_codes(qb, kb, vb), oracle.quantize(qb, kb, vb))
+    assert_codes_equal(gpu_codes(qb, kb, vb, qk_format), oracle.quantize(qb, kb, vb, qk_format=qk_format))
 
 
 def test_deterministic(device):

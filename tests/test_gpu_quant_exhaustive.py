@@ -8,7 +8,8 @@ the real quantize entry point and compare codes and scales with the oracle:
 
 - INT8 (Q path; K uses the same code): Q blocks of 128 tokens x 128 channels,
   each holding one amax value and a run of the BF16 values not above it, over
-  all 32639 positive finite amax values: about 1.07e9 pairs.
+  all 32639 positive finite amax values: about 1.07e9 pairs.  The same blocks
+  run through the FP8 Q/K format (E4M3 codes, block scale amax/448).
 - E4M3 (V path): one channel per amax value (255 heads x 128 channels), its
   65536 tokens holding every BF16 value not above it in magnitude.
 
@@ -33,12 +34,13 @@ def _values_up_to(a: int) -> np.ndarray:
     return np.concatenate([pos, neg])
 
 
-def test_int8_codes_all_bf16_pairs(device):
+@pytest.mark.parametrize("qk_format", ["int8", "fp8"])
+def test_q_codes_all_bf16_pairs(device, qk_format):
     import torch
     per = 128 * 128 - 1  # values per block besides its amax
     counts = (2 * AMAX_BITS + 1 + per - 1) // per
     nblk = int(counts.sum())
-    log(f"INT8 sweep: {nblk} Q blocks, {int((2 * AMAX_BITS + 1).sum())} pairs")
+    log(f"{qk_format} Q sweep: {nblk} Q blocks, {int((2 * AMAX_BITS + 1).sum())} pairs")
     blocks = np.zeros((nblk, 128 * 128), np.uint16)
     i = 0
     for a, c in zip(AMAX_BITS.tolist(), counts.tolist()):
@@ -53,13 +55,13 @@ def test_int8_codes_all_bf16_pairs(device):
     k = np.zeros((1, 1, 1, 128), np.uint16)
     v = np.zeros((1, 1, 1, 128), np.uint16)
     as_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)  # noqa: E731
-    got = sattn.unpack_host(sattn.quantize_qkv(as_dev(q), as_dev(k), as_dev(v)))
-    want = oracle.quantize(q, k, v)
+    got = sattn.unpack_host(sattn.quantize_qkv(as_dev(q), as_dev(k), as_dev(v), qk_format=qk_format))
+    want = oracle.quantize(q, k, v, qk_format=qk_format)
     assert np.array_equal(got["q_scale"].view(np.uint32), want["q_scale"].view(np.uint32))
     bad = got["q8"] != want["q8"]
     if bad.any():
         idx = np.argwhere(bad)[:5]
-        raise AssertionError(f"{int(bad.sum())} INT8 codes differ, first at {idx.tolist()}")
+        raise AssertionError(f"{int(bad.sum())} {qk_format} codes differ, first at {idx.tolist()}")
     log(f"  {q.size} codes and {nblk} block scales equal the oracle")
 
 
