@@ -47,9 +47,10 @@ def _load():
         lib.orc_quantize.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_int, P, P, P, P, P, P, P]
         lib.orc_quantize.restype = None
         lib.orc_attention_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
-                                           ctypes.c_float, I64, P, P, P, P]
+                                           ctypes.c_float, I64, P, P, P, P, P, P]
         lib.orc_attention_rows.restype = None
-        lib.orc_attention.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int, ctypes.c_float, P]
+        lib.orc_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int, ctypes.c_float,
+                                      P, P]
         lib.orc_attention.restype = None
         lib.orc_bruteforce.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
         lib.orc_bruteforce.restype = None
@@ -140,20 +141,25 @@ def _code_args(c: Dict[str, np.ndarray]):
 
 
 # ------------------------------------------------------------- attention ----
-def attention(codes: Dict[str, np.ndarray], softmax_scale: float) -> np.ndarray:
-    """Every row; BF16 bits, BSHD [B, Nq, H, 128]."""
+def attention(codes: Dict[str, np.ndarray], softmax_scale: float, return_lse: bool = False):
+    """Every row; BF16 bits, BSHD [B, Nq, H, 128].  With return_lse, also the
+    log-sum-exp of each row's logits before K smoothing, FP64 [B, H, Nq]."""
     B, H, Nq, _ = codes["q8"].shape
     Nkv = codes["k8"].shape[2]
     arrs = _code_args(codes)
     out = np.empty((B, Nq, H, D), np.uint16)
-    _load().orc_attention(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv,
-                          QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale, out.ctypes.data)
-    return out
+    lse = np.empty((B, H, Nq), np.float64) if return_lse else None
+    km = _c(codes["k_mean"], np.float32) if return_lse else None
+    _load().orc_attention(*(a.ctypes.data for a in arrs), None if km is None else km.ctypes.data,
+                          B, H, Nq, Nkv, QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale,
+                          out.ctypes.data, None if lse is None else lse.ctypes.data)
+    return (out, lse) if return_lse else out
 
 
 def attention_rows(codes: Dict[str, np.ndarray], softmax_scale: float,
-                   rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """rows: int64 [n, 3] of (b, h, i).  Returns (out BF16 [n,128], m [n], l [n])."""
+                   rows: np.ndarray, return_lse: bool = False):
+    """rows: int64 [n, 3] of (b, h, i).  Returns (out BF16 [n,128], m [n], l [n]),
+    and lse [n] (as in ``attention``) after them with return_lse."""
     B, H, Nq, _ = codes["q8"].shape
     Nkv = codes["k8"].shape[2]
     rows = _c(np.asarray(rows, dtype=np.int64).reshape(-1, 3), np.int64)
@@ -164,10 +170,14 @@ def attention_rows(codes: Dict[str, np.ndarray], softmax_scale: float,
     out = np.empty((n, D), np.uint16)
     m = np.empty(n, np.float64)
     l = np.empty(n, np.float64)
+    lse = np.empty(n, np.float64) if return_lse else None
+    km = _c(codes["k_mean"], np.float32) if return_lse else None
     _load().orc_attention_rows(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv,
                                QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale, n,
-                               rows.ctypes.data, out.ctypes.data, m.ctypes.data, l.ctypes.data)
-    return out, m, l
+                               rows.ctypes.data, None if km is None else km.ctypes.data,
+                               out.ctypes.data, m.ctypes.data, l.ctypes.data,
+                               None if lse is None else lse.ctypes.data)
+    return (out, m, l, lse) if return_lse else (out, m, l)
 
 
 def bruteforce(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale: float) -> np.ndarray:

@@ -23,6 +23,11 @@
  * per-block scale amax/448 (the same encoder and clamp as V), and exact
  * FP64 dot products of the decoded codes.
  *
+ * The attention entry points can also return each row's log-sum-exp (the
+ * float32 LSE kept beside the output in the FA4 autotuning page,
+ * "Validation"): that of the logits before K smoothing, i.e. the row's
+ * m + ln(l) plus the logit shift the smoothing removed.
+ *
  * Every loop runs in index order.  FP32 steps are single IEEE operations;
  * this file must be compiled with -ffp-contract=off and without fast-math.
  * Layouts: BF16 inputs are BSHD [B][N][H][128] contiguous (uint16 bit
@@ -292,13 +297,19 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   P8_j  = E4M3(fl32(448 * p_j))
  *   num_d = sum_j dec(P8_j) dec(V8[j,d])                (exact in FP64)
  *   o_d   = bf16(float(num_d * vs_d / (448 * l)))
- * `p` is caller scratch of Nkv floats.
+ *   lse   = m + ln(l) + softmax_scale * qs * sum_d qc_d * kmean_d   (FP64)
+ * lse is the log-sum-exp of the logits before K smoothing: the scores above
+ * use K - mean, and the last term adds back what that shift took from every
+ * logit of the row (qc_d: the Q code, decoded for FP8).  `p` is caller
+ * scratch of Nkv floats; `km` (the K mean of this (b, h)) and `lse_out` may
+ * be NULL when lse is not wanted.
  */
 static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                           const float* q_scale, const float* k_scale, const float* v_scale,
                           int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
-                          int64_t b, int64_t h, int64_t i,
-                          double* sc, float* p, uint16_t* out_row, double* m_out, double* l_out) {
+                          int64_t b, int64_t h, int64_t i, const float* km,
+                          double* sc, float* p, uint16_t* out_row, double* m_out, double* l_out,
+                          double* lse_out) {
   const int64_t bh = b * H + h;
   const int64_t nbq = nblocks(Nq), nbk = nblocks(Nkv);
   const int8_t* qi = q8 + (bh * Nq + i) * D;
@@ -339,14 +350,23 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
   }
   if (m_out) *m_out = m;
   if (l_out) *l_out = l;
+  if (lse_out) {
+    double shift = 0.0;
+    for (int d = 0; d < D; d++) {
+      const double qc = fmt == ORC_QK_FP8 ? orc_e4m3_decode((uint8_t)qi[d]) : (double)qi[d];
+      shift += qc * (double)km[d];
+    }
+    *lse_out = m + log(l) + (double)softmax_scale * qs * shift;
+  }
 }
 
-/* Selected rows: rows[3r..3r+2] = (b, h, i).  out: [nrows][128] BF16. */
+/* Selected rows: rows[3r..3r+2] = (b, h, i).  out: [nrows][128] BF16;
+ * m_out, l_out, lse_out: [nrows] or NULL (lse_out needs k_mean). */
 void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                         const float* q_scale, const float* k_scale, const float* v_scale,
                         int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
-                        int64_t nrows, const int64_t* rows,
-                        uint16_t* out, double* m_out, double* l_out) {
+                        int64_t nrows, const int64_t* rows, const float* k_mean,
+                        uint16_t* out, double* m_out, double* l_out, double* lse_out) {
   (void)B;
   #pragma omp parallel
   {
@@ -354,20 +374,25 @@ void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
     float* p = (float*)malloc(sizeof(float) * (size_t)Nkv);
     #pragma omp for schedule(dynamic)
     for (int64_t r = 0; r < nrows; r++) {
+      const int64_t bh = rows[3 * r] * H + rows[3 * r + 1];
       attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
-                    rows[3 * r], rows[3 * r + 1], rows[3 * r + 2], sc, p, out + r * D,
-                    m_out ? m_out + r : NULL, l_out ? l_out + r : NULL);
+                    rows[3 * r], rows[3 * r + 1], rows[3 * r + 2],
+                    k_mean ? k_mean + bh * D : NULL, sc, p, out + r * D,
+                    m_out ? m_out + r : NULL, l_out ? l_out + r : NULL,
+                    lse_out ? lse_out + r : NULL);
     }
     free(sc);
     free(p);
   }
 }
 
-/* Every row; out is BSHD [B][Nq][H][128] BF16. */
+/* Every row; out is BSHD [B][Nq][H][128] BF16; lse [B][H][Nq] or NULL
+ * (then k_mean may be NULL too). */
 void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                    const float* q_scale, const float* k_scale, const float* v_scale,
+                   const float* k_mean,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
-                   uint16_t* out) {
+                   uint16_t* out, double* lse) {
   #pragma omp parallel
   {
     double* sc = (double*)malloc(sizeof(double) * (size_t)Nkv);
@@ -377,7 +402,9 @@ void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
       for (int64_t h = 0; h < H; h++)
         for (int64_t i = 0; i < Nq; i++)
           attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
-                        b, h, i, sc, p, out + ((b * Nq + i) * H + h) * D, NULL, NULL);
+                        b, h, i, lse ? k_mean + (b * H + h) * D : NULL, sc, p,
+                        out + ((b * Nq + i) * H + h) * D, NULL, NULL,
+                        lse ? lse + (b * H + h) * Nq + i : NULL);
     free(sc);
     free(p);
   }
