@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--qk-format", choices=("int8", "fp8"), default="int8",
                     help="Q/K code format: INT8 (scale amax/127) or E4M3 (scale amax/448)")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="split-KV key ranges: 0 = the library's choice, 1 = none")
+    ap.add_argument("--lse", action="store_true", help="also write the per-row LSE")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -149,11 +152,14 @@ def main():
     work = torch.empty(wbytes, dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.B, cfg.Nq, cfg.H, 128), dtype=torch.bfloat16, device=dev)
     attend = sattn.fwd if cfg.Nq == cfg.Nkv else sattn.fwd_cross
+    swb, splits = sattn.fwd_workspace_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, args.num_splits)
+    split_ws = torch.empty(swb, dtype=torch.uint8, device=dev) if swb else None
 
     def step():
         p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work, qk_format=args.qk_format)
         ev[1].record()
-        attend(p, cfg.softmax_scale, out=out)
+        attend(p, cfg.softmax_scale, out=out, return_lse=args.lse, num_splits=args.num_splits,
+               workspace=split_ws)
         return p
 
     ev = [None, None, None]
@@ -195,7 +201,7 @@ def main():
         "dtype": "int8/fp8" if args.qk_format == "int8" else "fp8",
         "data": "synthetic",
         "config": dict(cfg.describe(), workload=cfg.name, softmax_scale=cfg.softmax_scale,
-                       qk_format=args.qk_format,
+                       qk_format=args.qk_format, kv_splits=splits, lse=args.lse,
                        step="sattn_quantize_qkv + " + ("sattn_fwd" if cfg.Nq == cfg.Nkv else "sattn_fwd_cross")),
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "attention_only": {"ms": round(t_attn, 4), "ms_min": round(t_attn_min, 4),

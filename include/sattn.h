@@ -61,6 +61,8 @@ extern "C" {
    32-bit work-item counts (2^22 blocks are 2^36 elements per tensor, more
    than one GPU's memory holds) */
 #define SATTN_MAX_BLOCKS (1 << 22)
+/* largest num_splits of the split-KV forward calls */
+#define SATTN_MAX_SPLITS 256
 
 typedef enum {
   SATTN_OK = 0,
@@ -137,10 +139,34 @@ sattn_status sattn_fwd_cross(const void* packed, size_t packed_bytes,
                              void* stream);
 
 /*
- * The same three calls with the Q/K code format as an argument (a format
- * outside sattn_qk_format is SATTN_ERR_INVALID_ARGUMENT).  The packed layout
- * and its size are the same for both formats; a packed buffer must be read
- * with the format it was written with (the library cannot tell them apart).
+ * The same three calls with the Q/K code format as an argument, and for the
+ * forward calls an optional LSE output and split-KV.
+ *
+ * qk_format: a sattn_qk_format; another value is SATTN_ERR_INVALID_ARGUMENT.
+ *   The packed layout and its size are the same for both formats; a packed
+ *   buffer must be read with the format it was written with (the library
+ *   cannot tell them apart).
+ *
+ * lse: NULL, or device FP32 [B][H][Nq] contiguous (4-byte aligned): per query
+ *   row the natural-log log-sum-exp of its logits before K smoothing,
+ *   m + ln(l) over the smoothed scores plus softmax_scale * qs *
+ *   sum_d qcode_d * kmean_d (the shift the smoothing removed).  It estimates
+ *   ln sum_j exp(softmax_scale * q . k_j), so outputs over disjoint key sets
+ *   merge as O = sum_i exp(lse_i - lse) O_i with lse = ln sum_i exp(lse_i)
+ *   (the float32 LSE and split-KV of the FA4 autotuning page, "Validation").
+ *
+ * num_splits: 1 = one workgroup sweeps all keys of its queries (the calls
+ *   without these arguments); k in [2, SATTN_MAX_SPLITS] = the key tiles are
+ *   cut into at most k ranges swept by separate workgroups, whose FP32
+ *   partial outputs and LSE are merged by a second kernel with the rule
+ *   above (for few queries and many keys, where one range per query tile
+ *   leaves most CUs idle); 0 = the library's choice (splits only launches
+ *   that would not fill the device once).  Other values are
+ *   SATTN_ERR_INVALID_ARGUMENT.
+ * workspace: device memory of at least the size sattn_fwd_workspace_bytes
+ *   returns for the same (B, H, Nq, Nkv, D, num_splits), 16-byte aligned,
+ *   caller-owned, not read before it is written; may be NULL (size 0) when
+ *   that size is 0.  Too small is SATTN_ERR_BUFFER_TOO_SMALL.
  */
 sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
                                    int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
@@ -150,11 +176,21 @@ sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
                                    void* workspace, size_t workspace_bytes, void* stream);
 sattn_status sattn_fwd_ex(const void* packed, size_t packed_bytes, int qk_format,
                           int64_t B, int64_t H, int64_t N, int64_t D, float softmax_scale,
-                          void* out, const int64_t* out_strides, void* stream);
+                          void* out, const int64_t* out_strides, float* lse, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
 sattn_status sattn_fwd_cross_ex(const void* packed, size_t packed_bytes, int qk_format,
                                 int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
                                 float softmax_scale, void* out, const int64_t* out_strides,
-                                void* stream);
+                                float* lse, int num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * Host-only size query for the split-KV workspace: bytes of workspace and
+ * the number of key ranges the forward calls will use for this problem and
+ * num_splits (either output pointer may be NULL).  Size 0 means no split.
+ */
+sattn_status sattn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                       int num_splits, size_t* workspace_bytes, int* splits_used);
 
 /*
  * Host-only inspection of a packed buffer (a host copy of it): writes the

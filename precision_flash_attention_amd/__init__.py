@@ -11,6 +11,13 @@ Entry points (same names as the C ABI):
     fwd(packed, softmax_scale, out)      -> Tensor   (self-attention)
     fwd_cross(packed, softmax_scale, out)-> Tensor   (cross-attention)
     attention(q, k, v, softmax_scale, out, qk_format=...)  (both stages)
+    fwd_workspace_bytes(B, H, Nq, Nkv, num_splits) -> (bytes, splits)
+
+The forward calls take ``return_lse`` (also return the FP32 [B, H, Nq]
+log-sum-exp of each row's logits, the FA4 autotuning page's float32 LSE) and
+``num_splits`` (split-KV: 1 = none, the default; 0 = the library's choice;
+k = at most k key ranges; the binding allocates the partials' workspace
+unless one is passed).
 
 ``qk_format`` is "int8" (INT8 Q/K codes, scale amax/127: the gfx1201 backend
 page's INT8/FP8/BF16 path) or "fp8" (E4M3 Q/K codes, scale amax/448: the
@@ -35,7 +42,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 __all__ = ["Packed", "SattnError", "QK_FORMATS", "abi_version", "packed_bytes", "quantize_qkv", "fwd",
-           "fwd_cross", "attention", "unpack_host", "e4m3_encode", "library_path"]
+           "fwd_cross", "attention", "fwd_workspace_bytes", "unpack_host", "e4m3_encode", "library_path"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libsattn.so")
@@ -80,13 +87,16 @@ def _load():
         lib.sattn_fwd_cross.argtypes = [_P, _SZ] + [_I64] * 5 + [ctypes.c_float, _P, _I64P, _P]
         lib.sattn_quantize_qkv_ex.argtypes = ([_P, _P, _P] + [_I64] * 5 + [_I64P] * 3 + [ctypes.c_int]
                                               + [_P, _SZ, _P, _SZ, _P])
-        lib.sattn_fwd_ex.argtypes = [_P, _SZ, ctypes.c_int] + [_I64] * 4 + [ctypes.c_float, _P, _I64P, _P]
+        lib.sattn_fwd_ex.argtypes = ([_P, _SZ, ctypes.c_int] + [_I64] * 4
+                                     + [ctypes.c_float, _P, _I64P, _P, ctypes.c_int, _P, _SZ, _P])
         lib.sattn_fwd_cross_ex.argtypes = ([_P, _SZ, ctypes.c_int] + [_I64] * 5
-                                           + [ctypes.c_float, _P, _I64P, _P])
+                                           + [ctypes.c_float, _P, _I64P, _P, ctypes.c_int, _P, _SZ, _P])
+        lib.sattn_fwd_workspace_bytes.argtypes = ([_I64] * 5 + [ctypes.c_int, ctypes.POINTER(_SZ),
+                                                                ctypes.POINTER(ctypes.c_int)])
         lib.sattn_unpack_host.argtypes = [_P, _SZ] + [_I64] * 5 + [_P] * 7
         lib.sattn_e4m3_encode.argtypes = [_P, _P, _I64, _P]
         for f in ("sattn_packed_bytes", "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_cross",
-                  "sattn_quantize_qkv_ex", "sattn_fwd_ex", "sattn_fwd_cross_ex",
+                  "sattn_quantize_qkv_ex", "sattn_fwd_ex", "sattn_fwd_cross_ex", "sattn_fwd_workspace_bytes",
                   "sattn_unpack_host", "sattn_e4m3_encode"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -203,34 +213,60 @@ def _out(p: Packed, out: Optional[torch.Tensor]) -> Tuple[torch.Tensor, torch.Te
     return out, o4
 
 
-def fwd(packed: Packed, softmax_scale: Optional[float] = None,
-        out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Self-attention (Nq == Nkv) from a packed buffer; BF16 output."""
+def fwd_workspace_bytes(B: int, H: int, Nq: int, Nkv: int, num_splits: int = 0) -> Tuple[int, int]:
+    """(split-KV workspace bytes, key ranges used) of a forward call."""
+    wb, used = _SZ(0), ctypes.c_int(0)
+    _check(_load().sattn_fwd_workspace_bytes(B, H, Nq, Nkv, HEAD_DIM, int(num_splits), ctypes.byref(wb),
+                                             ctypes.byref(used)), "sattn_fwd_workspace_bytes")
+    return int(wb.value), int(used.value)
+
+
+def _forward(name: str, packed: Packed, softmax_scale, out, return_lse: bool, num_splits: int,
+             workspace: Optional[torch.Tensor]):
     res, o4 = _out(packed, out)
+    dev = o4.device
+    lse = torch.empty((packed.B, packed.H, packed.Nq), dtype=torch.float32, device=dev) if return_lse else None
+    wb, _ = fwd_workspace_bytes(packed.B, packed.H, packed.Nq, packed.Nkv, num_splits)
+    if workspace is None and wb > 0:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wlen = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    common = (_scale(softmax_scale), o4.data_ptr(), _strides(o4), None if lse is None else lse.data_ptr(),
+              int(num_splits), wptr, wlen, _stream_ptr(dev))
+    lib = _load()
+    if name == "sattn_fwd":
+        st = lib.sattn_fwd_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+                              packed.B, packed.H, packed.Nq, HEAD_DIM, *common)
+    else:
+        st = lib.sattn_fwd_cross_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+                                    packed.B, packed.H, packed.Nq, packed.Nkv, HEAD_DIM, *common)
+    _check(st, name)
+    if not return_lse:
+        return res
+    return res, (lse[0] if packed.squeeze_batch else lse)
+
+
+def fwd(packed: Packed, softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        return_lse: bool = False, num_splits: int = 1, workspace: Optional[torch.Tensor] = None):
+    """Self-attention (Nq == Nkv) from a packed buffer; BF16 output (and the
+    FP32 LSE [B, H, Nq] with return_lse)."""
     if packed.Nq != packed.Nkv:
         raise NotImplementedError("fwd needs Nq == Nkv; use fwd_cross")
-    _check(_load().sattn_fwd_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
-                                packed.B, packed.H, packed.Nq, HEAD_DIM, _scale(softmax_scale),
-                                o4.data_ptr(), _strides(o4), _stream_ptr(o4.device)), "sattn_fwd")
-    return res
+    return _forward("sattn_fwd", packed, softmax_scale, out, return_lse, num_splits, workspace)
 
 
-def fwd_cross(packed: Packed, softmax_scale: Optional[float] = None,
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Cross-attention (any Nq, Nkv) from a packed buffer; BF16 output."""
-    res, o4 = _out(packed, out)
-    _check(_load().sattn_fwd_cross_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
-                                      packed.B, packed.H, packed.Nq, packed.Nkv, HEAD_DIM,
-                                      _scale(softmax_scale), o4.data_ptr(), _strides(o4),
-                                      _stream_ptr(o4.device)), "sattn_fwd_cross")
-    return res
+def fwd_cross(packed: Packed, softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+              return_lse: bool = False, num_splits: int = 1, workspace: Optional[torch.Tensor] = None):
+    """Cross-attention (any Nq, Nkv) from a packed buffer; BF16 output (and
+    the FP32 LSE [B, H, Nq] with return_lse)."""
+    return _forward("sattn_fwd_cross", packed, softmax_scale, out, return_lse, num_splits, workspace)
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
               causal: bool = False, attn_mask: Optional[torch.Tensor] = None,
               dropout_p: float = 0.0, cu_seqlens: Optional[torch.Tensor] = None,
-              qk_format: str = "int8") -> torch.Tensor:
+              qk_format: str = "int8", return_lse: bool = False, num_splits: int = 1):
     """Quantize and attend.  Rejects what this path does not compute."""
     if causal:
         raise NotImplementedError("causal attention is not supported")
@@ -242,8 +278,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise NotImplementedError("packed multi-sequence (cu_seqlens) inputs are not supported")
     p = quantize_qkv(q, k, v, qk_format=qk_format)
     if p.Nq == p.Nkv:
-        return fwd(p, softmax_scale, out)
-    return fwd_cross(p, softmax_scale, out)
+        return fwd(p, softmax_scale, out, return_lse=return_lse, num_splits=num_splits)
+    return fwd_cross(p, softmax_scale, out, return_lse=return_lse, num_splits=num_splits)
 
 
 def unpack_host(packed: Packed) -> Dict[str, "object"]:

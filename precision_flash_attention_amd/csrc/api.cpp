@@ -82,14 +82,52 @@ sattn_status launch_status(hipError_t e) { return e == hipSuccess ? SATTN_OK : S
 
 bool valid_format(int f) { return f == SATTN_QK_INT8 || f == SATTN_QK_FP8; }
 
+// Split-KV: how many key-tile ranges, and tiles per range, for a request of
+// num_splits (0: automatic).  The automatic choice splits only a launch whose
+// workgroups (B*H*ceil(Nq/256), one per CU at a time) would not fill the 256
+// CUs of an MI355X once, into as many ranges as fill them, each of at least
+// kMinTilesPerSplit key tiles.  Every range holds at least one tile.
+constexpr int64_t kCUs = 256;
+constexpr int64_t kMinTilesPerSplit = 8;
+
+struct Split {
+  int splits, tps;
+};
+
+Split resolve_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int num_splits) {
+  const int64_t nbk = sattn::nblocks(Nkv);
+  int64_t want = num_splits;
+  if (want == 0) {
+    const int64_t g1 = B * H * ((Nq + 255) / 256);
+    want = 1;
+    if (g1 < kCUs) {
+      want = kCUs / g1;
+      if (want > nbk / kMinTilesPerSplit) want = nbk / kMinTilesPerSplit;
+      if (want < 1) want = 1;
+    }
+  }
+  if (want > nbk) want = nbk;
+  const int64_t tps = (nbk + want - 1) / want;
+  return {(int)((nbk + tps - 1) / tps), (int)tps};
+}
+
 sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, int64_t B, int64_t H,
                         int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale, void* out,
-                        const int64_t* out_strides, void* stream, bool cross) {
+                        const int64_t* out_strides, float* lse, int num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream, bool cross) {
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
   if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
+  if (num_splits < 0 || num_splits > SATTN_MAX_SPLITS) return SATTN_ERR_INVALID_ARGUMENT;
   if (packed == nullptr || out == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(packed) || !aligned16(out)) return SATTN_ERR_INVALID_ARGUMENT;
+  if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return SATTN_ERR_INVALID_ARGUMENT;
+  const Split sp = resolve_splits(B, H, Nq, Nkv, num_splits);
+  if (sp.splits > 1) {
+    if (workspace == nullptr || !aligned16(workspace)) return SATTN_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < (size_t)sattn::split_workspace_bytes(sp.splits, B * H, Nq))
+      return SATTN_ERR_BUFFER_TOO_SMALL;
+  }
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return SATTN_ERR_INVALID_ARGUMENT;
   sattn::AttnArgs a;
   s = get_strides(out_strides, Nq, H, a.o_str);
@@ -102,6 +140,10 @@ sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, 
   a.softmax_scale = softmax_scale;
   a.out = static_cast<uint16_t*>(out);
   a.fp8qk = qk_format == SATTN_QK_FP8;
+  a.lse = lse;
+  a.splits = sp.splits;
+  a.tps = sp.tps;
+  a.workspace = static_cast<uint8_t*>(workspace);
   return launch_status(sattn::launch_attention(a, cross, static_cast<hipStream_t>(stream)));
 }
 
@@ -174,32 +216,45 @@ sattn_status sattn_quantize_qkv(const void* q, const void* k, const void* v,
                                stream);
 }
 
+sattn_status sattn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                       int num_splits, size_t* workspace_bytes, int* splits_used) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  if (num_splits < 0 || num_splits > SATTN_MAX_SPLITS) return SATTN_ERR_INVALID_ARGUMENT;
+  const Split sp = resolve_splits(B, H, Nq, Nkv, num_splits);
+  if (workspace_bytes) *workspace_bytes = (size_t)sattn::split_workspace_bytes(sp.splits, B * H, Nq);
+  if (splits_used) *splits_used = sp.splits;
+  return SATTN_OK;
+}
+
 sattn_status sattn_fwd_ex(const void* packed, size_t packed_bytes, int qk_format, int64_t B,
                           int64_t H, int64_t N, int64_t D, float softmax_scale, void* out,
-                          const int64_t* out_strides, void* stream) {
+                          const int64_t* out_strides, float* lse, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   return fwd_common(packed, packed_bytes, qk_format, B, H, N, N, D, softmax_scale, out, out_strides,
-                    stream, false);
+                    lse, num_splits, workspace, workspace_bytes, stream, false);
 }
 
 sattn_status sattn_fwd_cross_ex(const void* packed, size_t packed_bytes, int qk_format, int64_t B,
                                 int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale,
-                                void* out, const int64_t* out_strides, void* stream) {
+                                void* out, const int64_t* out_strides, float* lse, int num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_common(packed, packed_bytes, qk_format, B, H, Nq, Nkv, D, softmax_scale, out,
-                    out_strides, stream, true);
+                    out_strides, lse, num_splits, workspace, workspace_bytes, stream, true);
 }
 
 sattn_status sattn_fwd(const void* packed, size_t packed_bytes, int64_t B, int64_t H, int64_t N,
                        int64_t D, float softmax_scale, void* out, const int64_t* out_strides,
                        void* stream) {
   return sattn_fwd_ex(packed, packed_bytes, SATTN_QK_INT8, B, H, N, D, softmax_scale, out,
-                      out_strides, stream);
+                      out_strides, nullptr, 1, nullptr, 0, stream);
 }
 
 sattn_status sattn_fwd_cross(const void* packed, size_t packed_bytes, int64_t B, int64_t H,
                              int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale, void* out,
                              const int64_t* out_strides, void* stream) {
   return sattn_fwd_cross_ex(packed, packed_bytes, SATTN_QK_INT8, B, H, Nq, Nkv, D, softmax_scale,
-                            out, out_strides, stream);
+                            out, out_strides, nullptr, 1, nullptr, 0, stream);
 }
 
 sattn_status sattn_unpack_host(const void* packed_host, size_t packed_bytes, int64_t B, int64_t H,

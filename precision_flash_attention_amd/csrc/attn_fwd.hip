@@ -43,6 +43,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2_448 = 8.80735492205760410744f;
 constexpr int kStageBytes = 2 * (int)kTileBytes;  // K tile + V^T tile
 
@@ -53,11 +54,18 @@ struct AttnP {
   const float* qs;
   const float* ks;
   const float* vs;
+  const float* km;  // K mean [B*H][128]
   uint16_t* out;
   int64_t os0, os1, os2;
-  int64_t G;   // logical workgroups: B*H*mt
+  float* lse;    // [B*H][Nq] or null
+  float* opart;  // split partials: FP32 O [splits][B*H][Nq][128] (splits > 1)
+  float* lpart;  //   and their LSE [splits][B*H][Nq]
+  int64_t G;     // logical workgroups: B*H*splits*mt
+  int64_t BH;
   int H, Nq, Nkv, nbq, nbk, mt;
-  float sl2e;  // softmax_scale * log2(e)
+  int splits, tps;  // key-tile ranges [s*tps, min(nbk, (s+1)*tps)) per split s
+  float scale;      // softmax_scale
+  float sl2e;       // softmax_scale * log2(e)
 };
 
 __device__ inline int other_half_i(int x) {
@@ -126,8 +134,12 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   const int64_t wg = blockIdx.x;
   const int64_t L = (wg % 8) * (G8 / 8) + wg / 8;
   if (L >= p.G) return;
-  const int64_t bh = L / p.mt;
+  // logical order (b, h, split, query tile), query tile fastest: the
+  // workgroups sharing one K/V range are consecutive, hence on one XCD
+  const int64_t bhs = L / p.mt;
   const int mtile = (int)(L % p.mt);
+  const int64_t bh = bhs / p.splits;
+  const int split = (int)(bhs % p.splits);
   const int64_t b = bh / p.H, h = bh % p.H;
 
   const int tid = threadIdx.x;
@@ -139,7 +151,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   const bool isA = w < 4;
   const int q0 = mtile * BM + w * 32;
   const int qblk = q0 >> 7;
-  const int nbk = p.nbk;
+  // this workgroup's key tiles: [t0, t0 + nbk) of the head's p.nbk, nbk >= 1
+  const int t0 = split * p.tps;
+  const int nbk = min(p.nbk - t0, p.tps);
 
   v4i qf[4];
   float qscale = 0.0f;
@@ -154,9 +168,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     for (int m = 0; m < 4; ++m) qf[m] = v4i{0, 0, 0, 0};
   }
 
-  const uint8_t* kbase = p.k8 + bh * nbk * kTileBytes;
-  const uint8_t* vbase = p.v8 + bh * nbk * kTileBytes;
-  const float* ksc = p.ks + bh * nbk;
+  const uint8_t* kbase = p.k8 + (bh * p.nbk + t0) * kTileBytes;
+  const uint8_t* vbase = p.v8 + (bh * p.nbk + t0) * kTileBytes;
+  const float* ksc = p.ks + bh * p.nbk + t0;
 
   // Copy tile t into stage `stage`: wave `widx` of `nwaves` copies a
   // contiguous 32/nwaves KiB piece (within the K or the V^T tile).  The LDS
@@ -384,7 +398,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 
   if (!isA) barrier();  // group B lags one slot
   const int last = nbk - 1;
-  const int rem = p.Nkv - last * 128;
+  // keys in the last tile: the head's partial tail only in the last split
+  const int rem = t0 + nbk == p.nbk ? p.Nkv - (p.nbk - 1) * 128 : 128;
   auto step = [&](int t, bool do_pv, int kst) __attribute__((always_inline)) {
     mblock(t, do_pv, true, kst, 128);
     barrier();
@@ -411,28 +426,120 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   mblock(nbk, true, false, nbk % 3, 128);
   if (isA) barrier();
 
-  // ---- epilogue: O = acc * vs / l448 -> BF16
+  // ---- epilogue: O = acc * vs / l448 -> BF16 (or FP32 partials of a split)
   pin_accumulators(O);
   const float* vsc = p.vs + bh * 128;
   const float lt = l_run + other_half_f(l_run);
   const int q = q0 + l32;
+  // log-sum-exp of the row over this workgroup's keys, natural log:
+  // ln 2 * (m + log2(l448 / 448)) for the smoothed scores; and (when the
+  // caller asked for the LSE) the logit shift the K smoothing removed,
+  // softmax_scale * qs * sum_d qc_d kmean_d, from the Q codes this lane
+  // holds (channels 64 hh + [0, 64)).  Split partials carry no shift, so
+  // the merged output does not depend on whether the LSE is asked for.
+  float lse = 0.0f, shift = 0.0f;
+  if (p.lse != nullptr || p.splits > 1) lse = kLn2 * (m_run + log2f(lt) - kLog2_448);
+  if (p.lse != nullptr) {
+    const float* kmr = p.km + bh * 128 + 64 * hh;
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int word = qf[m][j];
+        float qc[4];
+        if constexpr (FP8QK) {
+          qc[0] = __builtin_amdgcn_cvt_f32_fp8(word, 0);
+          qc[1] = __builtin_amdgcn_cvt_f32_fp8(word, 1);
+          qc[2] = __builtin_amdgcn_cvt_f32_fp8(word, 2);
+          qc[3] = __builtin_amdgcn_cvt_f32_fp8(word, 3);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qc[e] = (float)(int8_t)(word >> (8 * e));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qc[e], kmr[16 * m + 4 * j + e], acc);
+      }
+    acc += other_half_f(acc);
+    shift = p.scale * qscale * acc;
+  }
   if (q < p.Nq) {
     const float inv = 1.0f / lt;
-    uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
+    if (p.splits == 1) {
+      uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * db + 8 * a + 4 * hh;
-        const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
-        const float o0 = O[db][4 * a + 0] * sv.x * inv;
-        const float o1 = O[db][4 * a + 1] * sv.y * inv;
-        const float o2 = O[db][4 * a + 2] * sv.z * inv;
-        const float o3 = O[db][4 * a + 3] * sv.w * inv;
-        *reinterpret_cast<uint2*>(orow + d0) =
-            make_uint2(bf16_rne(o0) | (bf16_rne(o1) << 16), bf16_rne(o2) | (bf16_rne(o3) << 16));
-      }
+        for (int a = 0; a < 4; ++a) {
+          const int d0 = 32 * db + 8 * a + 4 * hh;
+          const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
+          const float o0 = O[db][4 * a + 0] * sv.x * inv;
+          const float o1 = O[db][4 * a + 1] * sv.y * inv;
+          const float o2 = O[db][4 * a + 2] * sv.z * inv;
+          const float o3 = O[db][4 * a + 3] * sv.w * inv;
+          *reinterpret_cast<uint2*>(orow + d0) =
+              make_uint2(bf16_rne(o0) | (bf16_rne(o1) << 16), bf16_rne(o2) | (bf16_rne(o3) << 16));
+        }
+      if (p.lse != nullptr && hh == 0) p.lse[bh * p.Nq + q] = lse + shift;
+    } else {
+      const int64_t row = ((int64_t)split * p.BH + bh) * p.Nq + q;
+      float* orow = p.opart + row * 128;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d0 = 32 * db + 8 * a + 4 * hh;
+          const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
+          *reinterpret_cast<float4*>(orow + d0) =
+              make_float4(O[db][4 * a + 0] * sv.x * inv, O[db][4 * a + 1] * sv.y * inv,
+                          O[db][4 * a + 2] * sv.z * inv, O[db][4 * a + 3] * sv.w * inv);
+        }
+      if (hh == 0) p.lpart[row] = lse;
+      // the merge kernel adds the partials' lse to the shift left here
+      if (p.lse != nullptr && split == 0 && hh == 0) p.lse[bh * p.Nq + q] = shift;
+    }
   }
+}
+
+// Merge of split partials: row r = bh * Nq + q gets
+//   lse = ln sum_s exp(lse_s),  O = sum_s exp(lse_s - lse) O_s  -> BF16,
+// the log-sum-exp rule; the LSE output (if any) already holds the row's
+// smoothing shift, written by the attention kernel, and gets lse added.
+// 32 threads per row, 4 channels each.
+struct CombP {
+  const float* opart;
+  const float* lpart;
+  uint16_t* out;
+  float* lse;
+  int64_t os0, os1, os2;
+  int64_t rows;  // B*H*Nq
+  int H, Nq, splits;
+};
+
+__global__ __launch_bounds__(256) void k_combine(CombP p) {
+  const int64_t r = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (r >= p.rows) return;
+  const int c0 = (threadIdx.x & 31) * 4;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.lpart[s * p.rows + r]);
+  float wsum = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = 0; s < p.splits; ++s) {
+    const float w = __builtin_amdgcn_exp2f((p.lpart[s * p.rows + r] - mx) * kLog2e);
+    const float4 o = *reinterpret_cast<const float4*>(p.opart + (s * p.rows + r) * 128 + c0);
+    wsum += w;
+    acc.x = __builtin_fmaf(w, o.x, acc.x);
+    acc.y = __builtin_fmaf(w, o.y, acc.y);
+    acc.z = __builtin_fmaf(w, o.z, acc.z);
+    acc.w = __builtin_fmaf(w, o.w, acc.w);
+  }
+  const float inv = 1.0f / wsum;
+  const int64_t bh = r / p.Nq, q = r % p.Nq;
+  uint16_t* orow = p.out + (bh / p.H) * p.os0 + q * p.os1 + (bh % p.H) * p.os2 + c0;
+  *reinterpret_cast<uint2*>(orow) =
+      make_uint2(bf16_rne(acc.x * inv) | (bf16_rne(acc.y * inv) << 16),
+                 bf16_rne(acc.z * inv) | (bf16_rne(acc.w * inv) << 16));
+  if (p.lse != nullptr && c0 == 0) p.lse[r] += mx + kLn2 * log2f(wsum);
 }
 
 template <bool FP8QK>
@@ -460,20 +567,33 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   p.qs = reinterpret_cast<const float*>(a.packed + L.off_qs);
   p.ks = reinterpret_cast<const float*>(a.packed + L.off_ks);
   p.vs = reinterpret_cast<const float*>(a.packed + L.off_vs);
+  p.km = reinterpret_cast<const float*>(a.packed + L.off_km);
   p.out = a.out;
   p.os0 = a.o_str[0];
   p.os1 = a.o_str[1];
   p.os2 = a.o_str[2];
+  p.lse = a.lse;
+  p.BH = L.B * L.H;
+  p.splits = a.splits;
+  p.tps = a.tps;
+  p.opart = a.splits > 1 ? reinterpret_cast<float*>(a.workspace) : nullptr;
+  p.lpart = a.splits > 1 ? reinterpret_cast<float*>(a.workspace + split_opart_bytes(a.splits, p.BH, L.Nq))
+                         : nullptr;
   p.H = (int)L.H;
   p.Nq = (int)L.Nq;
   p.Nkv = (int)L.Nkv;
   p.nbq = (int)L.nbq;
   p.nbk = (int)L.nbk;
   p.mt = (int)((L.Nq + BM - 1) / BM);
-  p.G = L.B * L.H * p.mt;
+  p.G = p.BH * p.splits * p.mt;
+  p.scale = a.softmax_scale;
   p.sl2e = a.softmax_scale * kLog2e;
   const int64_t G8 = (p.G + 7) / 8 * 8;
   hipLaunchKernelGGL(attn_pp_kernel<FP8QK>, dim3((unsigned)G8), dim3(512), kLds, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  CombP c{p.opart, p.lpart, p.out, p.lse, p.os0, p.os1, p.os2, p.BH * L.Nq, p.H, p.Nq, p.splits};
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((c.rows + 7) / 8)), dim3(256), 0, stream, c);
   return hipGetLastError();
 }
 

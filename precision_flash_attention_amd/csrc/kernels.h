@@ -25,7 +25,20 @@ struct AttnArgs {
   uint16_t* out;
   int64_t o_str[3];
   bool fp8qk;  // the packed Q/K codes are E4M3
+  float* lse;  // [B][H][Nq] natural-log LSE of the logits before smoothing, or null
+  int splits;  // key-tile ranges swept by separate workgroups (1: no split)
+  int tps;     // key tiles per split
+  uint8_t* workspace;  // split partials (splits > 1), split_workspace_bytes() long
 };
+
+// Split-KV workspace: FP32 partial outputs [splits][B*H][Nq][128], then
+// their LSE [splits][B*H][Nq], each section 256-byte aligned.
+inline int64_t split_opart_bytes(int64_t splits, int64_t bh, int64_t nq) {
+  return align256(splits * bh * nq * 128 * 4);
+}
+inline int64_t split_workspace_bytes(int64_t splits, int64_t bh, int64_t nq) {
+  return splits <= 1 ? 0 : split_opart_bytes(splits, bh, nq) + align256(splits * bh * nq * 4);
+}
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream);

@@ -104,6 +104,9 @@ CONFIGS = {
     4: Config(4, "wan-like video self-attention", 1, 40, 32760, 32760, k_bias=2.0, outlier=8.0),
     5: Config(5, "long-sequence self-attention", 1, 24, 65520, 65520, q_dist=STUDENT4,
               k_dist=STUDENT4, k_bias=3.0),
+    # few queries against the Wan-like keys: 40 workgroups without split-KV
+    6: Config(6, "short-query long-key attention", 1, 40, 256, 32760, k_bias=2.0, outlier=8.0,
+              cross=True),
 }
 
 

@@ -135,6 +135,63 @@ def test_forward_validation(lib, cross):
     assert fwd_call(lib, cross) == DEVICE
 
 
+def fwd_ex(lib, cross, **kw):
+    a = dict(packed=ALIGNED, pbytes=1 << 40, fmt=0, B=1, H=2, Nq=256, Nkv=256, D=128, scale=0.088,
+             out=ALIGNED, os=None, lse=None, splits=1, ws=None, wbytes=0, stream=None)
+    a.update(kw)
+    tail = (ctypes.c_float(a["scale"]), a["out"], a["os"], a["lse"], a["splits"], a["ws"], a["wbytes"],
+            a["stream"])
+    if cross:
+        return lib.sattn_fwd_cross_ex(a["packed"], a["pbytes"], a["fmt"], a["B"], a["H"], a["Nq"], a["Nkv"],
+                                      a["D"], *tail)
+    return lib.sattn_fwd_ex(a["packed"], a["pbytes"], a["fmt"], a["B"], a["H"], a["Nq"], a["D"], *tail)
+
+
+def _split_sizes(B, H, Nq, Nkv, num_splits):
+    """Reference of the split rule as documented in include/sattn.h: the
+    automatic choice splits only launches of fewer than 256 workgroups, into
+    at most 256 // workgroups ranges of at least 8 tiles; every range holds a
+    tile; the partials take 128 FP32 + 1 FP32 per (range, row)."""
+    nbk = -(-Nkv // 128)
+    want = num_splits
+    if want == 0:
+        g1 = B * H * -(-Nq // 256)
+        want = max(1, min(256 // g1, nbk // 8)) if g1 < 256 else 1
+    want = min(want, nbk)
+    tps = -(-nbk // want)
+    used = -(-nbk // tps)
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return (0 if used == 1 else a(used * B * H * Nq * 512) + a(used * B * H * Nq * 4)), used
+
+
+@pytest.mark.parametrize("shape", [(1, 40, 256, 32760), (1, 40, 32760, 32760), (1, 2, 256, 256),
+                                   (2, 3, 64, 4608), (1, 1, 1, 1 << 20), (1, 40, 256, 1000), (3, 5, 700, 9000)])
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 7, 256])
+def test_split_workspace_sizes(shape, num_splits):
+    assert sattn.fwd_workspace_bytes(*shape, num_splits=num_splits) == _split_sizes(*shape, num_splits)
+
+
+def test_split_and_lse_validation(lib):
+    wb = ctypes.c_size_t()
+    assert lib.sattn_fwd_workspace_bytes(1, 2, 256, 256, 128, -1, ctypes.byref(wb), None) == INVALID
+    assert lib.sattn_fwd_workspace_bytes(1, 2, 256, 256, 128, 257, ctypes.byref(wb), None) == INVALID
+    assert lib.sattn_fwd_workspace_bytes(1, 2, 256, 256, 64, 1, ctypes.byref(wb), None) == UNSUPPORTED
+    big, used = sattn.fwd_workspace_bytes(1, 2, 256, 8192, num_splits=4)
+    assert used == 4 and big > 0
+    for cross in (False, True):
+        kw = dict(Nq=256, Nkv=8192) if cross else dict(Nq=8192, Nkv=8192)
+        size, _ = sattn.fwd_workspace_bytes(1, 2, kw["Nq"], kw["Nkv"], num_splits=4)
+        assert fwd_ex(lib, cross, splits=-1, **kw) == INVALID
+        assert fwd_ex(lib, cross, splits=257, **kw) == INVALID
+        assert fwd_ex(lib, cross, splits=4, **kw) == INVALID            # no workspace
+        assert fwd_ex(lib, cross, splits=4, ws=ALIGNED + 8, wbytes=size, **kw) == INVALID
+        assert fwd_ex(lib, cross, splits=4, ws=ALIGNED, wbytes=size - 1, **kw) == SMALL
+        assert fwd_ex(lib, cross, splits=4, ws=ALIGNED, wbytes=size, **kw) == DEVICE
+        assert fwd_ex(lib, cross, lse=ALIGNED + 2, **kw) == INVALID
+        assert fwd_ex(lib, cross, lse=ALIGNED + 4, **kw) == DEVICE
+        assert fwd_ex(lib, cross, splits=1, **kw) == DEVICE            # no split: no workspace needed
+
+
 def test_format_entry_points_validation(lib):
     """The _ex calls take the Q/K code format (0 = INT8, 1 = FP8); any other
     value is an invalid argument, checked before the device."""
@@ -143,13 +200,10 @@ def test_format_entry_points_validation(lib):
     for fmt, want in ((0, DEVICE), (1, DEVICE), (2, INVALID), (-1, INVALID)):
         assert lib.sattn_quantize_qkv_ex(q["q"], q["k"], q["v"], 1, 2, 256, 256, 128, st, None, None, fmt,
                                          ALIGNED, 1 << 40, ALIGNED, 1 << 40, None) == want, fmt
-        assert lib.sattn_fwd_ex(ALIGNED, 1 << 40, fmt, 1, 2, 256, 128, ctypes.c_float(0.088), ALIGNED,
-                                None, None) == want, fmt
-        assert lib.sattn_fwd_cross_ex(ALIGNED, 1 << 40, fmt, 1, 2, 256, 300, 128, ctypes.c_float(0.088),
-                                      ALIGNED, None, None) == want, fmt
+        assert fwd_ex(lib, False, fmt=fmt) == want, fmt
+        assert fwd_ex(lib, True, fmt=fmt) == want, fmt
     # the shape checks come first, as in the calls without a format
-    assert lib.sattn_fwd_ex(ALIGNED, 1 << 40, 1, 1, 2, 256, 64, ctypes.c_float(0.088), ALIGNED,
-                            None, None) == UNSUPPORTED
+    assert fwd_ex(lib, False, D=64) == UNSUPPORTED
     assert lib.sattn_quantize_qkv_ex(q["q"], q["k"], q["v"], 1, 2, 256, 256, 128, st, None, None, 1,
                                      ALIGNED, 100, ALIGNED, 1 << 40, None) == SMALL
     with pytest.raises(ValueError):

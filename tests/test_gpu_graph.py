@@ -17,10 +17,10 @@ pytestmark = pytest.mark.gpu
 def _eager(qd, kd, vd, packed, work, scale):
     p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work)
     attend = sattn.fwd if p.Nq == p.Nkv else sattn.fwd_cross
-    return attend(p, scale)
+    return attend(p, scale, num_splits=0)
 
 
-@pytest.mark.parametrize("Nq,Nkv", [(300, 300), (700, 200)])
+@pytest.mark.parametrize("Nq,Nkv", [(300, 300), (700, 200), (64, 4608)])
 def test_graph_replay_matches_eager(device, Nq, Nkv):
     import torch
     log(f"graph capture / replay, Nq={Nq} Nkv={Nkv}")
@@ -32,6 +32,11 @@ def test_graph_replay_matches_eager(device, Nq, Nkv):
     packed = torch.empty(pb, dtype=torch.uint8, device=device)
     work = torch.empty(wb, dtype=torch.uint8, device=device)
     out = torch.empty((1, Nq, 3, 128), dtype=torch.bfloat16, device=device)
+    # (64, 4608) runs split-KV (4 key ranges and the merge kernel); its
+    # workspace is allocated before the capture
+    swb, splits = sattn.fwd_workspace_bytes(1, 3, Nq, Nkv)
+    assert splits == (4 if Nkv == 4608 else 1)
+    sws = torch.empty(swb, dtype=torch.uint8, device=device) if swb else None
 
     # eager references on separate buffers, one per input set
     refs = []
@@ -45,14 +50,14 @@ def test_graph_replay_matches_eager(device, Nq, Nkv):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work)
-        (sattn.fwd if Nq == Nkv else sattn.fwd_cross)(p, scale, out=out)
+        (sattn.fwd if Nq == Nkv else sattn.fwd_cross)(p, scale, out=out, num_splits=0, workspace=sws)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work)
-        (sattn.fwd if Nq == Nkv else sattn.fwd_cross)(p, scale, out=out)
+        (sattn.fwd if Nq == Nkv else sattn.fwd_cross)(p, scale, out=out, num_splits=0, workspace=sws)
 
     for rep in range(6):
         i = rep % 3
