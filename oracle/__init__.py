@@ -52,6 +52,9 @@ def _load():
         lib.orc_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int, ctypes.c_float,
                                       P, P]
         lib.orc_attention.restype = None
+        lib.orc_attention_sparse.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
+                                             ctypes.c_float, P, P]
+        lib.orc_attention_sparse.restype = None
         lib.orc_bruteforce.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
         lib.orc_bruteforce.restype = None
         lib.orc_rounding_mode_is_nearest.argtypes = []
@@ -153,6 +156,26 @@ def attention(codes: Dict[str, np.ndarray], softmax_scale: float, return_lse: bo
     _load().orc_attention(*(a.ctypes.data for a in arrs), None if km is None else km.ctypes.data,
                           B, H, Nq, Nkv, QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale,
                           out.ctypes.data, None if lse is None else lse.ctypes.data)
+    return (out, lse) if return_lse else out
+
+
+def attention_sparse(codes: Dict[str, np.ndarray], softmax_scale: float, block_mask: np.ndarray,
+                     return_lse: bool = False):
+    """Block-sparse attention: query i attends key j iff
+    block_mask[b, h, i // 128, j // 128] (uint8/bool [B, H, nbq, nbk]).  As
+    ``attention`` over each row's allowed keys; a row without one gets
+    output 0 (and lse -inf)."""
+    B, H, Nq, _ = codes["q8"].shape
+    Nkv = codes["k8"].shape[2]
+    mask = _c(np.asarray(block_mask).astype(np.uint8), np.uint8)
+    assert mask.shape == (B, H, nblocks(Nq), nblocks(Nkv)), mask.shape
+    arrs = _code_args(codes)
+    out = np.empty((B, Nq, H, D), np.uint16)
+    lse = np.empty((B, H, Nq), np.float64) if return_lse else None
+    km = _c(codes["k_mean"], np.float32) if return_lse else None
+    _load().orc_attention_sparse(*(a.ctypes.data for a in arrs), None if km is None else km.ctypes.data,
+                                 mask.ctypes.data, B, H, Nq, Nkv, QK_FORMATS[codes.get("qk_format", "int8")],
+                                 softmax_scale, out.ctypes.data, None if lse is None else lse.ctypes.data)
     return (out, lse) if return_lse else out
 
 

@@ -303,11 +303,14 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * logit of the row (qc_d: the Q code, decoded for FP8).  `p` is caller
  * scratch of Nkv floats; `km` (the K mean of this (b, h)) and `lse_out` may
  * be NULL when lse is not wanted.
+ * `kmask` (block-sparse attention): NULL, or the row's allowed-key-block
+ * flags [nbk]; keys of other blocks take no part in m, l or the output.  A
+ * row with no allowed key gets output 0 and lse = -inf.
  */
 static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                           const float* q_scale, const float* k_scale, const float* v_scale,
                           int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
-                          int64_t b, int64_t h, int64_t i, const float* km,
+                          int64_t b, int64_t h, int64_t i, const float* km, const uint8_t* kmask,
                           double* sc, float* p, uint16_t* out_row, double* m_out, double* l_out,
                           double* lse_out) {
   const int64_t bh = b * H + h;
@@ -316,6 +319,10 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
   const double qs = (double)q_scale[bh * nbq + i / BLK];
   double m = -INFINITY;
   for (int64_t j = 0; j < Nkv; j++) {
+    if (kmask && !kmask[j / BLK]) {
+      sc[j] = -INFINITY;
+      continue;
+    }
     const int8_t* kj = k8 + (bh * Nkv + j) * D;
     double acc = 0.0;
     if (fmt == ORC_QK_FP8) {
@@ -330,6 +337,13 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
     double s = acc * qs * (double)k_scale[bh * nbk + j / BLK] * (double)softmax_scale;
     sc[j] = s;
     if (s > m) m = s;
+  }
+  if (m == -INFINITY) { /* no allowed key */
+    for (int d = 0; d < D; d++) out_row[d] = 0;
+    if (m_out) *m_out = m;
+    if (l_out) *l_out = 0.0;
+    if (lse_out) *lse_out = -INFINITY;
+    return;
   }
   double l = 0.0;
   for (int64_t j = 0; j < Nkv; j++) {
@@ -377,7 +391,7 @@ void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
       const int64_t bh = rows[3 * r] * H + rows[3 * r + 1];
       attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
                     rows[3 * r], rows[3 * r + 1], rows[3 * r + 2],
-                    k_mean ? k_mean + bh * D : NULL, sc, p, out + r * D,
+                    k_mean ? k_mean + bh * D : NULL, NULL, sc, p, out + r * D,
                     m_out ? m_out + r : NULL, l_out ? l_out + r : NULL,
                     lse_out ? lse_out + r : NULL);
     }
@@ -402,7 +416,37 @@ void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
       for (int64_t h = 0; h < H; h++)
         for (int64_t i = 0; i < Nq; i++)
           attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
-                        b, h, i, lse ? k_mean + (b * H + h) * D : NULL, sc, p,
+                        b, h, i, lse ? k_mean + (b * H + h) * D : NULL, NULL, sc, p,
+                        out + ((b * Nq + i) * H + h) * D, NULL, NULL,
+                        lse ? lse + (b * H + h) * Nq + i : NULL);
+    free(sc);
+    free(p);
+  }
+}
+
+/*
+ * Block-sparse attention: query i attends key j iff
+ * block_mask[b][h][i / 128][j / 128] != 0 (mask [B][H][nbq][nbk] uint8).
+ * Every row as in orc_attention over its allowed keys; rows without one get
+ * output 0 and lse -inf.  lse and k_mean may be NULL together.
+ */
+void orc_attention_sparse(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
+                          const float* q_scale, const float* k_scale, const float* v_scale,
+                          const float* k_mean, const uint8_t* block_mask,
+                          int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
+                          uint16_t* out, double* lse) {
+  const int64_t nbq = nblocks(Nq), nbk = nblocks(Nkv);
+  #pragma omp parallel
+  {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)Nkv);
+    float* p = (float*)malloc(sizeof(float) * (size_t)Nkv);
+    #pragma omp for collapse(3) schedule(dynamic)
+    for (int64_t b = 0; b < B; b++)
+      for (int64_t h = 0; h < H; h++)
+        for (int64_t i = 0; i < Nq; i++)
+          attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
+                        b, h, i, lse ? k_mean + (b * H + h) * D : NULL,
+                        block_mask + ((b * H + h) * nbq + i / BLK) * nbk, sc, p,
                         out + ((b * Nq + i) * H + h) * D, NULL, NULL,
                         lse ? lse + (b * H + h) * Nq + i : NULL);
     free(sc);

@@ -125,6 +125,20 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, B: Optional[int] = None
     return q, k, v
 
 
+def block_mask(B: int, H: int, Nq: int, Nkv: int, density: float, seed: int,
+               keep_diagonal: bool = True) -> np.ndarray:
+    """Seeded block-sparse pattern, uint8 [B, H, ceil(Nq/128), ceil(Nkv/128)]:
+    each (query block, key block) pair kept with probability `density`, and
+    (with keep_diagonal) the pairs on the block diagonal always, as a local
+    window would.  Drawn with numpy's PCG64 from `seed`."""
+    nbq, nbk = -(-Nq // 128), -(-Nkv // 128)
+    m = (np.random.default_rng(seed).random((B, H, nbq, nbk)) < density).astype(np.uint8)
+    if keep_diagonal:
+        d = np.arange(min(nbq, nbk))
+        m[:, :, d, d] = 1
+    return m
+
+
 def bf16_to_f32(x: np.ndarray) -> np.ndarray:
     """Exact widening of BF16 bit patterns."""
     return (x.astype(np.uint32) << 16).view(np.float32)
