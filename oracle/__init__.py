@@ -47,7 +47,7 @@ def _load():
         lib.orc_quantize.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_int, P, P, P, P, P, P, P]
         lib.orc_quantize.restype = None
         lib.orc_attention_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
-                                           ctypes.c_float, I64, P, P, P, P, P, P]
+                                           ctypes.c_float, I64, P, P, P, P, P, P, P]
         lib.orc_attention_rows.restype = None
         lib.orc_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int, ctypes.c_float,
                                       P, P]
@@ -180,9 +180,10 @@ def attention_sparse(codes: Dict[str, np.ndarray], softmax_scale: float, block_m
 
 
 def attention_rows(codes: Dict[str, np.ndarray], softmax_scale: float,
-                   rows: np.ndarray, return_lse: bool = False):
+                   rows: np.ndarray, return_lse: bool = False, block_mask: Optional[np.ndarray] = None):
     """rows: int64 [n, 3] of (b, h, i).  Returns (out BF16 [n,128], m [n], l [n]),
-    and lse [n] (as in ``attention``) after them with return_lse."""
+    and lse [n] (as in ``attention``) after them with return_lse.  With a
+    block_mask, the rows of ``attention_sparse``."""
     B, H, Nq, _ = codes["q8"].shape
     Nkv = codes["k8"].shape[2]
     rows = _c(np.asarray(rows, dtype=np.int64).reshape(-1, 3), np.int64)
@@ -195,9 +196,14 @@ def attention_rows(codes: Dict[str, np.ndarray], softmax_scale: float,
     l = np.empty(n, np.float64)
     lse = np.empty(n, np.float64) if return_lse else None
     km = _c(codes["k_mean"], np.float32) if return_lse else None
+    mask = None
+    if block_mask is not None:
+        mask = _c(np.asarray(block_mask).astype(np.uint8), np.uint8)
+        assert mask.shape == (B, H, nblocks(Nq), nblocks(Nkv)), mask.shape
     _load().orc_attention_rows(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv,
                                QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale, n,
                                rows.ctypes.data, None if km is None else km.ctypes.data,
+                               None if mask is None else mask.ctypes.data,
                                out.ctypes.data, m.ctypes.data, l.ctypes.data,
                                None if lse is None else lse.ctypes.data)
     return (out, m, l, lse) if return_lse else (out, m, l)

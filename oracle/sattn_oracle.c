@@ -375,13 +375,16 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
 }
 
 /* Selected rows: rows[3r..3r+2] = (b, h, i).  out: [nrows][128] BF16;
- * m_out, l_out, lse_out: [nrows] or NULL (lse_out needs k_mean). */
+ * m_out, l_out, lse_out: [nrows] or NULL (lse_out needs k_mean);
+ * block_mask: NULL (dense) or as in orc_attention_sparse. */
 void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                         const float* q_scale, const float* k_scale, const float* v_scale,
                         int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
                         int64_t nrows, const int64_t* rows, const float* k_mean,
+                        const uint8_t* block_mask,
                         uint16_t* out, double* m_out, double* l_out, double* lse_out) {
   (void)B;
+  const int64_t nbq = nblocks(Nq), nbk = nblocks(Nkv);
   #pragma omp parallel
   {
     double* sc = (double*)malloc(sizeof(double) * (size_t)Nkv);
@@ -391,7 +394,9 @@ void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
       const int64_t bh = rows[3 * r] * H + rows[3 * r + 1];
       attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
                     rows[3 * r], rows[3 * r + 1], rows[3 * r + 2],
-                    k_mean ? k_mean + bh * D : NULL, NULL, sc, p, out + r * D,
+                    k_mean ? k_mean + bh * D : NULL,
+                    block_mask ? block_mask + (bh * nbq + rows[3 * r + 2] / BLK) * nbk : NULL,
+                    sc, p, out + r * D,
                     m_out ? m_out + r : NULL, l_out ? l_out + r : NULL,
                     lse_out ? lse_out + r : NULL);
     }

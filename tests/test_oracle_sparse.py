@@ -131,3 +131,17 @@ def test_block_mask_generator():
     assert np.array_equal(m, testkit.block_mask(2, 3, 1000, 3000, 0.3, seed=7))
     assert np.all(m[:, :, np.arange(8), np.arange(8)] == 1)
     assert 0.25 < m.mean() < 0.4
+
+
+def test_rows_entry_matches_all_rows():
+    cfg = testkit.CONFIGS[3]
+    q, k, v = testkit.make_inputs(cfg, seed=6, B=2, H=2, Nq=300, Nkv=500)
+    c = oracle.quantize(q, k, v)
+    mask = testkit.block_mask(2, 2, 300, 500, 0.4, seed=11)
+    mask[1, 0, 2] = 0
+    o, lse = oracle.attention_sparse(c, SCALE, mask, return_lse=True)
+    rows = np.array([[0, 0, 0], [1, 1, 299], [1, 0, 260], [0, 1, 140]], np.int64)
+    o_r, _, _, lse_r = oracle.attention_rows(c, SCALE, rows, return_lse=True, block_mask=mask)
+    assert np.array_equal(lse_r, lse[rows[:, 0], rows[:, 1], rows[:, 2]])
+    assert np.array_equal(o_r, o[rows[:, 0], rows[:, 2], rows[:, 1]])
+    assert lse_r[2] == -np.inf
