@@ -193,6 +193,37 @@ sattn_status sattn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t
                                        int num_splits, size_t* workspace_bytes, int* splits_used);
 
 /*
+ * Block-sparse attention (the MHA v4 page's block-mask-to-ragged-LUT
+ * conversion and block-sparse reference; the sparse pipelines the AITER bump
+ * page measures).  Query i attends key j iff
+ * block_mask[b][h][i / 128][j / 128] != 0: 128-token blocks on both sides,
+ * the quantization blocks.  The quantizer does not see the mask; softmax, P
+ * rounding and the LSE run over each row's allowed keys; a row with no
+ * allowed key gets output 0 and lse -inf.
+ *
+ * sattn_block_lut_bytes: host-only size of the table for a problem.
+ * sattn_block_lut: block_mask = device uint8 [B][H][ceil(Nq/128)][ceil(Nkv/128)]
+ *   -> `lut` (device, caller-owned, 16-byte aligned, at least that size):
+ *   per tile of 256 queries (query blocks 2m and 2m+1) the ascending list of
+ *   the key blocks either attends, each entry marking which of the two does.
+ *   Launches one kernel on `stream`.  The table layout is the library's own;
+ *   pass it only to sattn_fwd_sparse with the same (B, H, Nq, Nkv).
+ * sattn_fwd_sparse: attention over the listed blocks (any Nq, Nkv), with
+ *   the conventions of sattn_fwd_cross_ex (qk_format, lse; no split-KV).
+ *   Work scales with the listed blocks.  Entries and counts are clamped to
+ *   the problem, so a damaged table gives wrong output, never an access
+ *   outside the buffers.
+ */
+sattn_status sattn_block_lut_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                   size_t* lut_bytes);
+sattn_status sattn_block_lut(const uint8_t* block_mask, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+                             int64_t D, void* lut, size_t lut_bytes, void* stream);
+sattn_status sattn_fwd_sparse(const void* packed, size_t packed_bytes, int qk_format,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                              float softmax_scale, const void* lut, size_t lut_bytes,
+                              void* out, const int64_t* out_strides, float* lse, void* stream);
+
+/*
  * Host-only inspection of a packed buffer (a host copy of it): writes the
  * canonical layouts
  *   q8 [B,H,Nq,128] and k8 [B,H,Nkv,128] (INT8 codes, or E4M3 bits for

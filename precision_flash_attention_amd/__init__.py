@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
     fwd_cross(packed, softmax_scale, out)-> Tensor   (cross-attention)
     attention(q, k, v, softmax_scale, out, qk_format=...)  (both stages)
     fwd_workspace_bytes(B, H, Nq, Nkv, num_splits) -> (bytes, splits)
+    block_lut(block_mask, Nq, Nkv)       -> BlockLut (block-sparse table)
+    fwd_sparse(packed, lut, softmax_scale, out)  (block-sparse attention)
 
 The forward calls take ``return_lse`` (also return the FP32 [B, H, Nq]
 log-sum-exp of each row's logits, the FA4 autotuning page's float32 LSE) and
@@ -42,7 +44,8 @@ from typing import Dict, Optional, Tuple
 import torch
 
 __all__ = ["Packed", "SattnError", "QK_FORMATS", "abi_version", "packed_bytes", "quantize_qkv", "fwd",
-           "fwd_cross", "attention", "fwd_workspace_bytes", "unpack_host", "e4m3_encode", "library_path"]
+           "fwd_cross", "attention", "fwd_workspace_bytes", "BlockLut", "block_lut_bytes", "block_lut",
+           "fwd_sparse", "unpack_host", "e4m3_encode", "library_path"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libsattn.so")
@@ -93,10 +96,15 @@ def _load():
                                            + [ctypes.c_float, _P, _I64P, _P, ctypes.c_int, _P, _SZ, _P])
         lib.sattn_fwd_workspace_bytes.argtypes = ([_I64] * 5 + [ctypes.c_int, ctypes.POINTER(_SZ),
                                                                 ctypes.POINTER(ctypes.c_int)])
+        lib.sattn_block_lut_bytes.argtypes = [_I64] * 5 + [ctypes.POINTER(_SZ)]
+        lib.sattn_block_lut.argtypes = [_P] + [_I64] * 5 + [_P, _SZ, _P]
+        lib.sattn_fwd_sparse.argtypes = ([_P, _SZ, ctypes.c_int] + [_I64] * 5
+                                         + [ctypes.c_float, _P, _SZ, _P, _I64P, _P, _P])
         lib.sattn_unpack_host.argtypes = [_P, _SZ] + [_I64] * 5 + [_P] * 7
         lib.sattn_e4m3_encode.argtypes = [_P, _P, _I64, _P]
         for f in ("sattn_packed_bytes", "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_cross",
                   "sattn_quantize_qkv_ex", "sattn_fwd_ex", "sattn_fwd_cross_ex", "sattn_fwd_workspace_bytes",
+                  "sattn_block_lut_bytes", "sattn_block_lut", "sattn_fwd_sparse",
                   "sattn_unpack_host", "sattn_e4m3_encode"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -260,6 +268,60 @@ def fwd_cross(packed: Packed, softmax_scale: Optional[float] = None, out: Option
     """Cross-attention (any Nq, Nkv) from a packed buffer; BF16 output (and
     the FP32 LSE [B, H, Nq] with return_lse)."""
     return _forward("sattn_fwd_cross", packed, softmax_scale, out, return_lse, num_splits, workspace)
+
+
+@dataclass
+class BlockLut:
+    """Output of block_lut: a device table in the library's layout."""
+    buf: torch.Tensor
+    B: int
+    H: int
+    Nq: int
+    Nkv: int
+
+
+def block_lut_bytes(B: int, H: int, Nq: int, Nkv: int) -> int:
+    n = _SZ(0)
+    _check(_load().sattn_block_lut_bytes(B, H, Nq, Nkv, HEAD_DIM, ctypes.byref(n)), "sattn_block_lut_bytes")
+    return int(n.value)
+
+
+def block_lut(block_mask: torch.Tensor, Nq: int, Nkv: int, out: Optional[torch.Tensor] = None) -> BlockLut:
+    """Block mask [B, H, ceil(Nq/128), ceil(Nkv/128)] (bool or uint8, device;
+    nonzero = attend) -> the table fwd_sparse reads."""
+    if not isinstance(block_mask, torch.Tensor) or block_mask.device.type != "cuda":
+        raise ValueError("block_mask must be a device tensor")
+    if block_mask.dim() != 4:
+        raise ValueError("block_mask must be [B, H, ceil(Nq/128), ceil(Nkv/128)]")
+    B, H, nbq, nbk = block_mask.shape
+    if (nbq, nbk) != ((Nq + 127) // 128, (Nkv + 127) // 128):
+        raise ValueError(f"block_mask has {nbq} x {nbk} blocks, expected "
+                         f"{(Nq + 127) // 128} x {(Nkv + 127) // 128}")
+    m = block_mask.to(torch.uint8).contiguous()
+    n = block_lut_bytes(B, H, Nq, Nkv)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=m.device)
+    _check(_load().sattn_block_lut(m.data_ptr(), B, H, Nq, Nkv, HEAD_DIM, out.data_ptr(),
+                                   out.numel() * out.element_size(), _stream_ptr(m.device)), "sattn_block_lut")
+    return BlockLut(out, B, H, Nq, Nkv)
+
+
+def fwd_sparse(packed: Packed, lut: BlockLut, softmax_scale: Optional[float] = None,
+               out: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Block-sparse attention over the blocks the table lists; BF16 output
+    (and the FP32 LSE [B, H, Nq], -inf on rows without keys, with return_lse)."""
+    if (lut.B, lut.H, lut.Nq, lut.Nkv) != (packed.B, packed.H, packed.Nq, packed.Nkv):
+        raise ValueError("the block table was made for another problem shape")
+    res, o4 = _out(packed, out)
+    dev = o4.device
+    lse = torch.empty((packed.B, packed.H, packed.Nq), dtype=torch.float32, device=dev) if return_lse else None
+    _check(_load().sattn_fwd_sparse(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+                                    packed.B, packed.H, packed.Nq, packed.Nkv, HEAD_DIM, _scale(softmax_scale),
+                                    lut.buf.data_ptr(), lut.buf.numel(), o4.data_ptr(), _strides(o4),
+                                    None if lse is None else lse.data_ptr(), _stream_ptr(dev)), "sattn_fwd_sparse")
+    if not return_lse:
+        return res
+    return res, (lse[0] if packed.squeeze_batch else lse)
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -114,7 +114,8 @@ Split resolve_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int num_spli
 sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, int64_t B, int64_t H,
                         int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale, void* out,
                         const int64_t* out_strides, float* lse, int num_splits, void* workspace,
-                        size_t workspace_bytes, void* stream, bool cross) {
+                        size_t workspace_bytes, void* stream, bool cross,
+                        const void* lut = nullptr, size_t lut_bytes = 0) {
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
   if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
@@ -122,7 +123,13 @@ sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, 
   if (packed == nullptr || out == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(packed) || !aligned16(out)) return SATTN_ERR_INVALID_ARGUMENT;
   if (lse != nullptr && ((uintptr_t)lse & 3u) != 0) return SATTN_ERR_INVALID_ARGUMENT;
-  const Split sp = resolve_splits(B, H, Nq, Nkv, num_splits);
+  const Split sp = lut != nullptr ? Split{1, (int)sattn::nblocks(Nkv)}
+                                  : resolve_splits(B, H, Nq, Nkv, num_splits);
+  if (lut != nullptr) {
+    if (!aligned16(lut)) return SATTN_ERR_INVALID_ARGUMENT;
+    if (lut_bytes < (size_t)sattn::block_lut_bytes(B, H, Nq, sattn::nblocks(Nkv)))
+      return SATTN_ERR_BUFFER_TOO_SMALL;
+  }
   if (sp.splits > 1) {
     if (workspace == nullptr || !aligned16(workspace)) return SATTN_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < (size_t)sattn::split_workspace_bytes(sp.splits, B * H, Nq))
@@ -144,6 +151,14 @@ sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, 
   a.splits = sp.splits;
   a.tps = sp.tps;
   a.workspace = static_cast<uint8_t*>(workspace);
+  a.lut_counts = nullptr;
+  a.lut_entries = nullptr;
+  if (lut != nullptr) {
+    const uint8_t* l = static_cast<const uint8_t*>(lut);
+    a.lut_counts = reinterpret_cast<const int32_t*>(l);
+    a.lut_entries = reinterpret_cast<const uint32_t*>(
+        l + sattn::lut_counts_bytes(B * H * ((Nq + 255) / 256)));
+  }
   return launch_status(sattn::launch_attention(a, cross, static_cast<hipStream_t>(stream)));
 }
 
@@ -241,6 +256,37 @@ sattn_status sattn_fwd_cross_ex(const void* packed, size_t packed_bytes, int qk_
                                 void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_common(packed, packed_bytes, qk_format, B, H, Nq, Nkv, D, softmax_scale, out,
                     out_strides, lse, num_splits, workspace, workspace_bytes, stream, true);
+}
+
+sattn_status sattn_block_lut_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                   size_t* lut_bytes) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  if (lut_bytes) *lut_bytes = (size_t)sattn::block_lut_bytes(B, H, Nq, sattn::nblocks(Nkv));
+  return SATTN_OK;
+}
+
+sattn_status sattn_block_lut(const uint8_t* block_mask, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+                             int64_t D, void* lut, size_t lut_bytes, void* stream) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  if (block_mask == nullptr || lut == nullptr || !aligned16(lut)) return SATTN_ERR_INVALID_ARGUMENT;
+  if (lut_bytes < (size_t)sattn::block_lut_bytes(B, H, Nq, sattn::nblocks(Nkv)))
+    return SATTN_ERR_BUFFER_TOO_SMALL;
+  s = check_device();
+  if (s != SATTN_OK) return s;
+  const Layout L = sattn::make_layout(B, H, Nq, Nkv);
+  return launch_status(sattn::launch_block_lut(block_mask, L, static_cast<uint8_t*>(lut),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+sattn_status sattn_fwd_sparse(const void* packed, size_t packed_bytes, int qk_format, int64_t B,
+                              int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float softmax_scale,
+                              const void* lut, size_t lut_bytes, void* out,
+                              const int64_t* out_strides, float* lse, void* stream) {
+  if (lut == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
+  return fwd_common(packed, packed_bytes, qk_format, B, H, Nq, Nkv, D, softmax_scale, out, out_strides,
+                    lse, 1, nullptr, 0, stream, true, lut, lut_bytes);
 }
 
 sattn_status sattn_fwd(const void* packed, size_t packed_bytes, int64_t B, int64_t H, int64_t N,

@@ -73,6 +73,8 @@ struct AttnP {
   float* lse;    // [B*H][Nq] or null
   float* opart;  // split partials: FP32 O [splits][B*H][Nq][128] (splits > 1)
   float* lpart;  //   and their LSE [splits][B*H][Nq]
+  const int32_t* lut_counts;    // block-sparse: key tiles per query tile [B*H*mt]
+  const uint32_t* lut_entries;  //   and their entries [B*H*mt][nbk]
   int64_t G;     // logical workgroups: B*H*splits*mt
   int64_t BH;
   int H, Nq, Nkv, nbq, nbk, mt;
@@ -137,7 +139,7 @@ constexpr float kMagicF = 12582912.0f;
 // FP8QK: Q and K codes are E4M3 (the FP8/FP8/BF16 format): S^T comes from
 // v_mfma_scale_f32_32x32x64_f8f6f4 in FP32, the K operands being the same
 // LDS reads taken two 16-byte chunks per MFMA.
-template <bool FP8QK>
+template <bool FP8QK, bool SPARSE>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int NW = 8;
@@ -164,9 +166,40 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   const bool isA = w < 4;
   const int q0 = mtile * BM + w * 32;
   const int qblk = q0 >> 7;
-  // this workgroup's key tiles: [t0, t0 + nbk) of the head's p.nbk, nbk >= 1
+  // this workgroup's key tiles: [t0, t0 + nbk) of the head's p.nbk, nbk >= 1;
+  // block-sparse: the nbk >= 0 tiles its LUT entries list (t0 = 0)
   const int t0 = split * p.tps;
-  const int nbk = min(p.nbk - t0, p.tps);
+  int nbk = min(p.nbk - t0, p.tps);
+  const __attribute__((address_space(4))) uint32_t* ent = nullptr;
+  if constexpr (SPARSE) {
+    // scalar loads; a count or index out of range is clamped, so a
+    // malformed table cannot make the kernel read outside the head
+    const __attribute__((address_space(4))) int32_t* cnt =
+        (const __attribute__((address_space(4))) int32_t*)(p.lut_counts);
+    nbk = min(max(cnt[L], 0), p.nbk);
+    ent = (const __attribute__((address_space(4))) uint32_t*)(p.lut_entries) + L * p.nbk;
+    if (nbk == 0) {  // no allowed key for either query block: O = 0, lse = -inf
+      const int q = q0 + l32;
+      if (q < p.Nq) {
+        uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) *reinterpret_cast<uint4*>(orow + 64 * hh + 8 * a) = make_uint4(0, 0, 0, 0);
+        if (p.lse != nullptr && hh == 0) p.lse[bh * p.Nq + q] = -__builtin_inff();
+      }
+      return;
+    }
+  }
+  // key tile of local step t, and whether this wave group's query block
+  // attends it (entry bit 30: the tile's first 128 queries, waves 0-3; bit
+  // 31: the second 128, waves 4-7)
+  auto tile_of = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return min((int)(ent[t] & 0x3FFFFFFFu), p.nbk - 1);
+    else return t;
+  };
+  auto group_attends = [&](int t) __attribute__((always_inline)) -> bool {
+    if constexpr (SPARSE) return ((ent[t] >> (isA ? 30 : 31)) & 1u) != 0;
+    else return true;
+  };
 
   v4i qf[4];
   float qscale = 0.0f;
@@ -193,8 +226,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   auto copy_tile = [&](int t, int stage, int widx, int nwaves) __attribute__((always_inline)) {
     const int per = 2048 / nwaves;  // 16-byte pieces per wave
     const int c0 = widx * per;      // first piece, wave-uniform
-    const uint8_t* src = (c0 < 1024 ? kbase + (int64_t)t * kTileBytes + c0 * 16
-                                    : vbase + (int64_t)t * kTileBytes + (c0 - 1024) * 16) + lane * 16;
+    const int64_t tile = tile_of(t);
+    const uint8_t* src = (c0 < 1024 ? kbase + tile * kTileBytes + c0 * 16
+                                    : vbase + tile * kTileBytes + (c0 - 1024) * 16) + lane * 16;
     uint8_t* dst = smem + stage * kStageBytes + c0 * 16;
     for (int i = 0; i < per / 256; ++i) {
       copy_to_lds_off<0>(src + i * 4096, dst + i * 4096);
@@ -215,7 +249,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   v16i S0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) S0[r] = kMagicBits;
-  float c_cur = 0.0f;  // dequant scale of the tile whose S is held
+  float c_cur = 0.0f;       // dequant scale of the tile whose S is held
+  bool masked_cur = false;  // block-sparse: that tile is masked for this group
   // The K block scales are read through the constant address space, which
   // makes these uniform loads scalar (s_load, counted by lgkmcnt).  A vector
   // load here would be followed by a vmcnt wait that also waits for the
@@ -230,7 +265,12 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   // get the bits of -inf.  As an integer that is below every biased score,
   // so the row maximum ignores it; as a float it gives exp2(fma(-inf, c, nb))
   // = 0.  The MFMA-issuing wave waits for these S values here, once per sweep.
-  auto mblock = [&](int t, bool do_pv, bool do_s, int kst, int mask_rem) __attribute__((always_inline)) {
+  // mask_all (block-sparse): this wave group's query block does not attend
+  // tile t.  The scores are left as they are; the V phase then keeps the row
+  // maximum and gives every p the exponent -inf (two wave-uniform selects
+  // instead of rewriting 64 score registers).
+  auto mblock = [&](int t, bool do_pv, bool do_s, int kst, int mask_rem,
+                    bool mask_all) __attribute__((always_inline)) {
     // the MFMA-issuing wave of the SIMD gets issue priority over its partner
     __builtin_amdgcn_s_setprio(2);
     if (isA && t >= 1 && t + 1 < nbk) copy_tile(t + 1, kst == 2 ? 0 : kst + 1, w, 4);
@@ -307,7 +347,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      c_cur = qscale * ksc4[t] * p.sl2e;
+      c_cur = qscale * ksc4[tile_of(t)] * p.sl2e;
+      if constexpr (SPARSE) masked_cur = mask_all;
       if (mask_rem < 128) {
         // the first masked key offset of this lane half; the empty asm before
         // each comparison keeps the 64 lane masks from all being computed up
@@ -351,6 +392,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       mx = max(mx, other_half_i(mx));
       mt = (__int_as_float(mx) - kMagicF) * c;
     }
+    if constexpr (SPARSE) {
+      if (masked_cur) mt = -__builtin_inff();  // the row maximum stays
+    }
     const float mnew = fmaxf(m_run, mt);
     if (__any(mnew > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
@@ -362,8 +406,16 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     }
     m_run = mnew;
     // exponent argument fma(S_f, c, nb) = (score - m) log2 e + log2 448; for
-    // INT8 codes the float view of S carries the bias 1.5 * 2^23
-    const float nb = FP8QK ? kLog2_448 - mnew : __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew);
+    // INT8 codes the float view of S carries the bias 1.5 * 2^23, folded into
+    // nb.  Rounding that nb to FP32 moves the tile's reference point by up to
+    // 0.75 c; the block-sparse instance, whose rows may see few tiles, instead
+    // subtracts the bias from each score (exact) at one more VALU operation
+    // per score.
+    constexpr bool kFoldBias = !FP8QK && !SPARSE;
+    float nb = kFoldBias ? __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew) : kLog2_448 - mnew;
+    if constexpr (SPARSE) {
+      if (masked_cur) nb = -__builtin_inff();  // every p of the tile is 0
+    }
     float ls[4];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -374,7 +426,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(S[kb][r0 + i]), c, nb));
+          const float sf = __int_as_float(S[kb][r0 + i]);
+          pv[i] = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(FP8QK || kFoldBias ? sf : sf - kMagicF, c, nb));
           // the first term starts the sum (p >= 0, so 0 + p == p)
           ls[i] = (g == 0 && j == 0) ? pv[i] : ls[i] + pv[i];
         }
@@ -412,9 +466,11 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   if (!isA) barrier();  // group B lags one slot
   const int last = nbk - 1;
   // keys in the last tile: the head's partial tail only in the last split
-  const int rem = t0 + nbk == p.nbk ? p.Nkv - (p.nbk - 1) * 128 : 128;
+  // (block-sparse: when the head's last tile is listed, it is listed last)
+  int rem = t0 + nbk == p.nbk ? p.Nkv - (p.nbk - 1) * 128 : 128;
+  if constexpr (SPARSE) rem = tile_of(last) == p.nbk - 1 ? p.Nkv - (p.nbk - 1) * 128 : 128;
   auto step = [&](int t, bool do_pv, int kst) __attribute__((always_inline)) {
-    mblock(t, do_pv, true, kst, 128);
+    mblock(t, do_pv, true, kst, 128, SPARSE && !group_attends(t));
     barrier();
     vblock();
     if (isA) wait_loads();
@@ -431,12 +487,12 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     step(t + 2, true, 0);
   }
   for (; t < last; ++t) step(t, true, t % 3);
-  mblock(last, last > 0, true, last % 3, rem);
+  mblock(last, last > 0, true, last % 3, rem, SPARSE && !group_attends(last));
   barrier();
   vblock();
   if (isA) wait_loads();
   barrier();
-  mblock(nbk, true, false, nbk % 3, 128);
+  mblock(nbk, true, false, nbk % 3, 128, false);
   if (isA) barrier();
 
   // ---- epilogue: O = acc * vs / l448 -> BF16 (or FP32 partials of a split)
@@ -477,7 +533,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     shift = p.scale * qscale * acc;
   }
   if (q < p.Nq) {
-    const float inv = 1.0f / lt;
+    // (block-sparse: a row whose query block attends none of the listed
+    // tiles has l = 0, O = 0 and lse = -inf)
+    const float inv = SPARSE && lt == 0.0f ? 0.0f : 1.0f / lt;
     if (p.splits == 1) {
       uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
 #pragma unroll
@@ -555,7 +613,43 @@ __global__ __launch_bounds__(256) void k_combine(CombP p) {
   if (p.lse != nullptr && c0 == 0) p.lse[r] += mx + kLn2 * log2f(wsum);
 }
 
-template <bool FP8QK>
+// Block mask [B][H][nbq][nbk] (nonzero = attend) -> per query tile of 256
+// rows (query blocks 2m, 2m+1) the ascending list of key tiles either block
+// attends, each entry the tile index | bit 30 (block 2m attends) | bit 31
+// (block 2m+1 attends), and the list's length.  One wave per query tile: 64
+// key tiles per step, compacted in order through a ballot.
+struct LutP {
+  const uint8_t* mask;
+  int32_t* counts;
+  uint32_t* entries;
+  int64_t G;  // B*H*mt
+  int nbq, nbk, mt;
+};
+
+__global__ __launch_bounds__(256) void k_block_lut(LutP p) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= p.G) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = g / p.mt;
+  const int qb0 = 2 * (int)(g % p.mt);
+  const bool two = qb0 + 1 < p.nbq;
+  const uint8_t* m0 = p.mask + (bh * p.nbq + qb0) * p.nbk;
+  const uint8_t* m1 = m0 + p.nbk;
+  uint32_t* out = p.entries + g * p.nbk;
+  int count = 0;
+  for (int k0 = 0; k0 < p.nbk; k0 += 64) {
+    const int kb = k0 + lane;
+    const bool a0 = kb < p.nbk && m0[kb] != 0;
+    const bool a1 = kb < p.nbk && two && m1[kb] != 0;
+    const uint64_t any = __ballot(a0 || a1);
+    const int pos = count + __popcll(any & ((1ull << lane) - 1ull));
+    if (a0 || a1) out[pos] = (uint32_t)kb | (a0 ? 1u << 30 : 0u) | (a1 ? 1u << 31 : 0u);
+    count += __popcll(any);
+  }
+  if (lane == 0) p.counts[g] = count;
+}
+
+template <bool FP8QK, bool SPARSE>
 hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
   constexpr int BM = 256;
@@ -568,7 +662,7 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDev || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<FP8QK>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<FP8QK, SPARSE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDev) attr_set[dev] = true;
@@ -602,7 +696,9 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   p.scale = a.softmax_scale;
   p.sl2e = a.softmax_scale * kLog2e;
   const int64_t G8 = (p.G + 7) / 8 * 8;
-  hipLaunchKernelGGL(attn_pp_kernel<FP8QK>, dim3((unsigned)G8), dim3(512), kLds, stream, p);
+  p.lut_counts = a.lut_counts;
+  p.lut_entries = a.lut_entries;
+  hipLaunchKernelGGL((attn_pp_kernel<FP8QK, SPARSE>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   CombP c{p.opart, p.lpart, p.out, p.lse, p.os0, p.os1, p.os2, p.BH * L.Nq, p.H, p.Nq, p.splits};
@@ -614,7 +710,22 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
   (void)cross;
-  return a.fp8qk ? launch_pp<true>(a, stream) : launch_pp<false>(a, stream);
+  if (a.lut_counts != nullptr)
+    return a.fp8qk ? launch_pp<true, true>(a, stream) : launch_pp<false, true>(a, stream);
+  return a.fp8qk ? launch_pp<true, false>(a, stream) : launch_pp<false, false>(a, stream);
+}
+
+hipError_t launch_block_lut(const uint8_t* mask, const Layout& L, uint8_t* lut, hipStream_t stream) {
+  LutP p;
+  p.mask = mask;
+  p.mt = (int)((L.Nq + 255) / 256);
+  p.G = L.B * L.H * p.mt;
+  p.nbq = (int)L.nbq;
+  p.nbk = (int)L.nbk;
+  p.counts = reinterpret_cast<int32_t*>(lut);
+  p.entries = reinterpret_cast<uint32_t*>(lut + lut_counts_bytes(p.G));
+  hipLaunchKernelGGL(k_block_lut, dim3((unsigned)((p.G + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace sattn

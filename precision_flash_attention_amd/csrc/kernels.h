@@ -29,7 +29,19 @@ struct AttnArgs {
   int splits;  // key-tile ranges swept by separate workgroups (1: no split)
   int tps;     // key tiles per split
   uint8_t* workspace;  // split partials (splits > 1), split_workspace_bytes() long
+  const int32_t* lut_counts;    // block-sparse LUT (null: dense), from launch_block_lut
+  const uint32_t* lut_entries;
 };
+
+// Block-sparse LUT: per query tile of 256 rows (g = (b*H + h)*mt + m, mt =
+// ceil(Nq/256)) an int32 count, then [g][nbk] uint32 entries (key tile |
+// bit 30 if query block 2m attends it | bit 31 if block 2m+1 does),
+// ascending; each section 256-byte aligned.
+inline int64_t lut_counts_bytes(int64_t g) { return align256(g * 4); }
+inline int64_t block_lut_bytes(int64_t B, int64_t H, int64_t Nq, int64_t nbk) {
+  const int64_t g = B * H * ((Nq + 255) / 256);
+  return lut_counts_bytes(g) + align256(g * nbk * 4);
+}
 
 // Split-KV workspace: FP32 partial outputs [splits][B*H][Nq][128], then
 // their LSE [splits][B*H][Nq], each section 256-byte aligned.
@@ -43,5 +55,6 @@ inline int64_t split_workspace_bytes(int64_t splits, int64_t bh, int64_t nq) {
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
+hipError_t launch_block_lut(const uint8_t* mask, const Layout& L, uint8_t* lut, hipStream_t stream);
 
 }  // namespace sattn

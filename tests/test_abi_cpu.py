@@ -192,6 +192,44 @@ def test_split_and_lse_validation(lib):
         assert fwd_ex(lib, cross, splits=1, **kw) == DEVICE            # no split: no workspace needed
 
 
+def _lut_bytes(B, H, Nq, Nkv):
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    g = B * H * -(-Nq // 256)
+    return a(4 * g) + a(4 * g * -(-Nkv // 128))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 300, 700), (2, 40, 32760, 32760), (1, 1, 1, 1), (3, 5, 257, 129)])
+def test_block_lut_sizes(shape):
+    assert sattn.block_lut_bytes(*shape) == _lut_bytes(*shape)
+
+
+def test_sparse_validation(lib):
+    n = _lut_bytes(1, 2, 300, 700)
+    assert lib.sattn_block_lut(None, 1, 2, 300, 700, 128, ALIGNED, n, None) == INVALID
+    assert lib.sattn_block_lut(ALIGNED, 1, 2, 300, 700, 128, None, n, None) == INVALID
+    assert lib.sattn_block_lut(ALIGNED, 1, 2, 300, 700, 128, ALIGNED + 4, n, None) == INVALID
+    assert lib.sattn_block_lut(ALIGNED, 1, 2, 300, 700, 128, ALIGNED, n - 1, None) == SMALL
+    assert lib.sattn_block_lut(ALIGNED, 1, 2, 300, 700, 64, ALIGNED, n, None) == UNSUPPORTED
+    assert lib.sattn_block_lut(ALIGNED, 1, 2, 300, 700, 128, ALIGNED, n, None) == DEVICE
+
+    def fs(**kw):
+        a = dict(packed=ALIGNED, pbytes=1 << 40, fmt=0, D=128, scale=0.088, lut=ALIGNED, lbytes=n,
+                 out=ALIGNED, lse=None)
+        a.update(kw)
+        return lib.sattn_fwd_sparse(a["packed"], a["pbytes"], a["fmt"], 1, 2, 300, 700, a["D"],
+                                    ctypes.c_float(a["scale"]), a["lut"], a["lbytes"], a["out"], None,
+                                    a["lse"], None)
+    assert fs(lut=None) == INVALID
+    assert fs(lut=ALIGNED + 8) == INVALID
+    assert fs(lbytes=n - 1) == SMALL
+    assert fs(fmt=3) == INVALID
+    assert fs(D=64) == UNSUPPORTED
+    assert fs(scale=0.0) == INVALID
+    assert fs(lse=ALIGNED + 1) == INVALID
+    assert fs(pbytes=10) == SMALL
+    assert fs() == DEVICE
+
+
 def test_format_entry_points_validation(lib):
     """The _ex calls take the Q/K code format (0 = INT8, 1 = FP8); any other
     value is an invalid argument, checked before the device."""
