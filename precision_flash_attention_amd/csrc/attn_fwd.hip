@@ -251,6 +251,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   for (int r = 0; r < 16; ++r) S0[r] = kMagicBits;
   float c_cur = 0.0f;       // dequant scale of the tile whose S is held
   bool masked_cur = false;  // block-sparse: that tile is masked for this group
+  bool pv_skip = false;     // block-sparse: the P registers belong to a masked tile
   // The K block scales are read through the constant address space, which
   // makes these uniform loads scalar (s_load, counted by lgkmcnt).  A vector
   // load here would be followed by a vmcnt wait that also waits for the
@@ -266,15 +267,15 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   // so the row maximum ignores it; as a float it gives exp2(fma(-inf, c, nb))
   // = 0.  The MFMA-issuing wave waits for these S values here, once per sweep.
   // mask_all (block-sparse): this wave group's query block does not attend
-  // tile t.  The scores are left as they are; the V phase then keeps the row
-  // maximum and gives every p the exponent -inf (two wave-uniform selects
-  // instead of rewriting 64 score registers).
+  // tile t.  The group skips the tile's score MFMAs, its V phase and its PV
+  // MFMAs (wave-uniform branches): the row maximum, the row sum and O stay
+  // as they are.
   auto mblock = [&](int t, bool do_pv, bool do_s, int kst, int mask_rem,
                     bool mask_all) __attribute__((always_inline)) {
     // the MFMA-issuing wave of the SIMD gets issue priority over its partner
     __builtin_amdgcn_s_setprio(2);
     if (isA && t >= 1 && t + 1 < nbk) copy_tile(t + 1, kst == 2 ? 0 : kst + 1, w, 4);
-    if (do_pv) {
+    if (do_pv && !(SPARSE && pv_skip)) {
       const uint8_t* Vs = smem + (kst == 0 ? 2 : kst - 1) * kStageBytes + kTileBytes;  // stage of t-1
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -299,7 +300,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    if (do_s) {
+    if constexpr (SPARSE) {
+      if (do_s) masked_cur = mask_all;
+    }
+    if (do_s && !(SPARSE && mask_all)) {
       const uint8_t* Ks = smem + kst * kStageBytes;
       v4i kf[4][4];
 #pragma unroll
@@ -348,7 +352,6 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       c_cur = qscale * ksc4[tile_of(t)] * p.sl2e;
-      if constexpr (SPARSE) masked_cur = mask_all;
       if (mask_rem < 128) {
         // the first masked key offset of this lane half; the empty asm before
         // each comparison keeps the 64 lane masks from all being computed up
@@ -368,6 +371,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 
   // ---- V(t): online softmax of S -> P, conditional rescale of O
   auto vblock = [&]() __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      pv_skip = masked_cur;
+      if (masked_cur) return;
+    }
     // c = 0 (an all-zero Q or K block: every score of the tile is 0) would
     // turn masked keys' -inf into NaN; the smallest normal float gives the
     // same exponent arguments for the valid keys (its products stay far
@@ -392,9 +399,6 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       mx = max(mx, other_half_i(mx));
       mt = (__int_as_float(mx) - kMagicF) * c;
     }
-    if constexpr (SPARSE) {
-      if (masked_cur) mt = -__builtin_inff();  // the row maximum stays
-    }
     const float mnew = fmaxf(m_run, mt);
     if (__any(mnew > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
@@ -413,9 +417,6 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     // per score.
     constexpr bool kFoldBias = !FP8QK && !SPARSE;
     float nb = kFoldBias ? __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew) : kLog2_448 - mnew;
-    if constexpr (SPARSE) {
-      if (masked_cur) nb = -__builtin_inff();  // every p of the tile is 0
-    }
     float ls[4];
 #pragma unroll
     for (int g = 0; g < 2; ++g)

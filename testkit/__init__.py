@@ -79,6 +79,7 @@ class Config:
     k_bias: float = 0.0
     outlier: float = 1.0
     cross: bool = False
+    density: Optional[float] = None  # block-sparse: block_mask density (None: dense)
 
     @property
     def seed(self) -> int:
@@ -86,15 +87,28 @@ class Config:
 
     @property
     def flops(self) -> int:
-        return 4 * self.B * self.H * self.Nq * self.Nkv * D
+        """4 * (query, key) pairs attended * D: all pairs, or those the
+        workload's block mask allows."""
+        if self.density is None:
+            return 4 * self.B * self.H * self.Nq * self.Nkv * D
+        m = self.block_mask().astype(np.int64)
+        rows = np.minimum(128, self.Nq - 128 * np.arange(m.shape[2]))
+        keys = np.minimum(128, self.Nkv - 128 * np.arange(m.shape[3]))
+        return int(4 * D * np.einsum("bhqk,q,k->", m, rows, keys))
+
+    def block_mask(self) -> np.ndarray:
+        return block_mask(self.B, self.H, self.Nq, self.Nkv, self.density, seed=self.seed)
 
     @property
     def softmax_scale(self) -> float:
         return 1.0 / np.sqrt(128.0)
 
     def describe(self) -> dict:
-        return {"workload": self.name, "B": self.B, "H": self.H, "Nq": self.Nq, "Nkv": self.Nkv,
-                "D": D, "seed": self.seed}
+        d = {"workload": self.name, "B": self.B, "H": self.H, "Nq": self.Nq, "Nkv": self.Nkv,
+             "D": D, "seed": self.seed}
+        if self.density is not None:
+            d["block_density"] = self.density
+        return d
 
 
 CONFIGS = {
@@ -107,6 +121,9 @@ CONFIGS = {
     # few queries against the Wan-like keys: 40 workgroups without split-KV
     6: Config(6, "short-query long-key attention", 1, 40, 256, 32760, k_bias=2.0, outlier=8.0,
               cross=True),
+    # the Wan-like workload under a seeded block mask keeping half the blocks
+    7: Config(7, "wan-like video block-sparse attention", 1, 40, 32760, 32760, k_bias=2.0,
+              outlier=8.0, density=0.5),
 }
 
 
