@@ -44,15 +44,15 @@ def _load():
         lib.orc_e4m3_encode_bits.restype = None
         lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
         lib.orc_f32_to_bf16.restype = ctypes.c_uint16
-        lib.orc_quantize.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_int, P, P, P, P, P, P, P]
+        lib.orc_quantize.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_int, P, P, P, P, P, P, P, P]
         lib.orc_quantize.restype = None
         lib.orc_attention_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
-                                           ctypes.c_float, I64, P, P, P, P, P, P, P]
+                                           ctypes.c_float, I64, P, P, P, P, P, P, P, P]
         lib.orc_attention_rows.restype = None
-        lib.orc_attention.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int, ctypes.c_float,
-                                      P, P]
+        lib.orc_attention.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
+                                      ctypes.c_float, P, P]
         lib.orc_attention.restype = None
-        lib.orc_attention_sparse.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
+        lib.orc_attention_sparse.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int,
                                              ctypes.c_float, P, P]
         lib.orc_attention_sparse.restype = None
         lib.orc_bruteforce.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
@@ -113,14 +113,19 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
 QK_FORMATS = {"int8": 0, "fp8": 1}
 
 
-def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray, qk_format: str = "int8") -> Dict[str, np.ndarray]:
+def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray, qk_format: str = "int8",
+             q_smooth: bool = False) -> Dict[str, np.ndarray]:
     """Codes and scales; qk_format "int8" (scale amax/127) or "fp8" (E4M3
-    bit patterns, scale amax/448) for Q and smoothed K."""
+    bit patterns, scale amax/448) for Q and smoothed K.  With q_smooth, Q is
+    smoothed per 128-token block (codes of q - block mean) and "q_mean"
+    [B, H, nbq, 128] holds the means; the attention functions then add the
+    Delta-S term back to every score."""
     fmt = QK_FORMATS[qk_format]
     B, Nq, H, d = q.shape
     Nkv = k.shape[1]
     assert d == D and k.shape == (B, Nkv, H, D) and v.shape == (B, Nkv, H, D)
     q, k, v = (_c(t, np.uint16) for t in (q, k, v))
+    qm = np.empty((B, H, nblocks(Nq), D), np.float32) if q_smooth else None
     r = {
         "q8": np.empty((B, H, Nq, D), np.int8),
         "k8": np.empty((B, H, Nkv, D), np.int8),
@@ -132,9 +137,17 @@ def quantize(q: np.ndarray, k: np.ndarray, v: np.ndarray, qk_format: str = "int8
     }
     _load().orc_quantize(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Nq, Nkv, fmt,
                          *(r[n].ctypes.data for n in ("q8", "k8", "v8", "q_scale", "k_scale",
-                                                      "v_scale", "k_mean")))
+                                                      "v_scale", "k_mean")),
+                         None if qm is None else qm.ctypes.data)
     r["qk_format"] = qk_format
+    if q_smooth:
+        r["q_mean"] = qm
     return r
+
+
+def _qmean_ptr(c: Dict[str, np.ndarray]):
+    qm = c.get("q_mean")
+    return None if qm is None else _c(qm, np.float32)
 
 
 def _code_args(c: Dict[str, np.ndarray]):
@@ -153,8 +166,9 @@ def attention(codes: Dict[str, np.ndarray], softmax_scale: float, return_lse: bo
     out = np.empty((B, Nq, H, D), np.uint16)
     lse = np.empty((B, H, Nq), np.float64) if return_lse else None
     km = _c(codes["k_mean"], np.float32) if return_lse else None
+    qm = _qmean_ptr(codes)
     _load().orc_attention(*(a.ctypes.data for a in arrs), None if km is None else km.ctypes.data,
-                          B, H, Nq, Nkv, QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale,
+                          None if qm is None else qm.ctypes.data, B, H, Nq, Nkv, QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale,
                           out.ctypes.data, None if lse is None else lse.ctypes.data)
     return (out, lse) if return_lse else out
 
@@ -173,8 +187,9 @@ def attention_sparse(codes: Dict[str, np.ndarray], softmax_scale: float, block_m
     out = np.empty((B, Nq, H, D), np.uint16)
     lse = np.empty((B, H, Nq), np.float64) if return_lse else None
     km = _c(codes["k_mean"], np.float32) if return_lse else None
+    qm = _qmean_ptr(codes)
     _load().orc_attention_sparse(*(a.ctypes.data for a in arrs), None if km is None else km.ctypes.data,
-                                 mask.ctypes.data, B, H, Nq, Nkv, QK_FORMATS[codes.get("qk_format", "int8")],
+                                 None if qm is None else qm.ctypes.data, mask.ctypes.data, B, H, Nq, Nkv, QK_FORMATS[codes.get("qk_format", "int8")],
                                  softmax_scale, out.ctypes.data, None if lse is None else lse.ctypes.data)
     return (out, lse) if return_lse else out
 
@@ -200,9 +215,11 @@ def attention_rows(codes: Dict[str, np.ndarray], softmax_scale: float,
     if block_mask is not None:
         mask = _c(np.asarray(block_mask).astype(np.uint8), np.uint8)
         assert mask.shape == (B, H, nblocks(Nq), nblocks(Nkv)), mask.shape
+    qm = _qmean_ptr(codes)
     _load().orc_attention_rows(*(a.ctypes.data for a in arrs), B, H, Nq, Nkv,
                                QK_FORMATS[codes.get("qk_format", "int8")], softmax_scale, n,
                                rows.ctypes.data, None if km is None else km.ctypes.data,
+                               None if qm is None else qm.ctypes.data,
                                None if mask is None else mask.ctypes.data,
                                out.ctypes.data, m.ctypes.data, l.ctypes.data,
                                None if lse is None else lse.ctypes.data)

@@ -216,26 +216,38 @@ static int64_t nblocks(int64_t n) { return (n + BLK - 1) / BLK; }
 void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt,
                   int8_t* q8, int8_t* k8, uint8_t* v8,
-                  float* q_scale, float* k_scale, float* v_scale, float* k_mean) {
+                  float* q_scale, float* k_scale, float* v_scale, float* k_mean,
+                  float* q_mean) {
   const int64_t nbq = nblocks(Nq), nbk = nblocks(Nkv);
   #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int64_t b = 0; b < B; b++) {
     for (int64_t h = 0; h < H; h++) {
       const int64_t bh = b * H + h;
-      /* --- Q --- */
+      /* --- Q (with q_mean: smoothed per block, q' = fl32(q - block mean)) --- */
       for (int64_t t = 0; t < nbq; t++) {
         int64_t n0 = t * BLK, n1 = n0 + BLK < Nq ? n0 + BLK : Nq;
+        float qm[D];
+        for (int d = 0; d < D; d++) {
+          qm[d] = 0.0f;
+          if (q_mean) {
+            float tot = 0.0f;
+            for (int64_t n = n0; n < n1; n++) tot = tot + bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]);
+            qm[d] = tot / (float)(n1 - n0);
+            q_mean[(bh * nbq + t) * D + d] = qm[d];
+          }
+        }
         float amax = 0.0f;
         for (int64_t n = n0; n < n1; n++)
           for (int d = 0; d < D; d++) {
-            float x = fabsf(bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]));
+            float x = fabsf(bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]) - qm[d]);
             if (x > amax) amax = x;
           }
         float s = amax / qk_max(fmt);
         q_scale[bh * nbq + t] = s;
         for (int64_t n = n0; n < n1; n++)
           for (int d = 0; d < D; d++)
-            q8[(bh * Nq + n) * D + d] = qk_code(bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]), s, fmt);
+            q8[(bh * Nq + n) * D + d] =
+                qk_code(bf16_to_f32(q[((b * Nq + n) * H + h) * D + d]) - qm[d], s, fmt);
       }
       /* --- K mean --- */
       float mean[D];
@@ -298,6 +310,11 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   num_d = sum_j dec(P8_j) dec(V8[j,d])                (exact in FP64)
  *   o_d   = bf16(float(num_d * vs_d / (448 * l)))
  *   lse   = m + ln(l) + softmax_scale * qs * sum_d qc_d * kmean_d   (FP64)
+ * With Q smoothing (`qm`, the row's block mean, non-NULL) the score gains
+ * the Delta-S term that restores the block mean,
+ *   s_j  += qm . kc_j * ks_blk(j) * softmax_scale         (FP64; kc: the K
+ *                                                        code, decoded)
+ * and the lse shift becomes softmax_scale * (qs * qc + qm) . kmean.
  * lse is the log-sum-exp of the logits before K smoothing: the scores above
  * use K - mean, and the last term adds back what that shift took from every
  * logit of the row (qc_d: the Q code, decoded for FP8).  `p` is caller
@@ -310,7 +327,8 @@ void orc_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                           const float* q_scale, const float* k_scale, const float* v_scale,
                           int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
-                          int64_t b, int64_t h, int64_t i, const float* km, const uint8_t* kmask,
+                          int64_t b, int64_t h, int64_t i, const float* km, const float* qm,
+                          const uint8_t* kmask,
                           double* sc, float* p, uint16_t* out_row, double* m_out, double* l_out,
                           double* lse_out) {
   const int64_t bh = b * H + h;
@@ -334,7 +352,17 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
       for (int d = 0; d < D; d++) ia += (int32_t)qi[d] * (int32_t)kj[d];
       acc = (double)ia;
     }
-    double s = acc * qs * (double)k_scale[bh * nbk + j / BLK] * (double)softmax_scale;
+    if (qm) {
+      double ds = 0.0;
+      for (int d = 0; d < D; d++) {
+        const double kc = fmt == ORC_QK_FP8 ? orc_e4m3_decode((uint8_t)kj[d]) : (double)kj[d];
+        ds += (double)qm[d] * kc;
+      }
+      acc = acc * qs + ds;  /* in units of the K scale */
+    } else {
+      acc = acc * qs;
+    }
+    double s = acc * (double)k_scale[bh * nbk + j / BLK] * (double)softmax_scale;
     sc[j] = s;
     if (s > m) m = s;
   }
@@ -368,20 +396,21 @@ static void attention_row(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
     double shift = 0.0;
     for (int d = 0; d < D; d++) {
       const double qc = fmt == ORC_QK_FP8 ? orc_e4m3_decode((uint8_t)qi[d]) : (double)qi[d];
-      shift += qc * (double)km[d];
+      shift += (qc * qs + (qm ? (double)qm[d] : 0.0)) * (double)km[d];
     }
-    *lse_out = m + log(l) + (double)softmax_scale * qs * shift;
+    *lse_out = m + log(l) + (double)softmax_scale * shift;
   }
 }
 
 /* Selected rows: rows[3r..3r+2] = (b, h, i).  out: [nrows][128] BF16;
  * m_out, l_out, lse_out: [nrows] or NULL (lse_out needs k_mean);
- * block_mask: NULL (dense) or as in orc_attention_sparse. */
+ * block_mask: NULL (dense) or as in orc_attention_sparse; q_mean: NULL, or
+ * the Q block means [B][H][nbq][128] of a Q-smoothed quantization. */
 void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                         const float* q_scale, const float* k_scale, const float* v_scale,
                         int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
                         int64_t nrows, const int64_t* rows, const float* k_mean,
-                        const uint8_t* block_mask,
+                        const float* q_mean, const uint8_t* block_mask,
                         uint16_t* out, double* m_out, double* l_out, double* lse_out) {
   (void)B;
   const int64_t nbq = nblocks(Nq), nbk = nblocks(Nkv);
@@ -395,6 +424,7 @@ void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
       attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
                     rows[3 * r], rows[3 * r + 1], rows[3 * r + 2],
                     k_mean ? k_mean + bh * D : NULL,
+                    q_mean ? q_mean + (bh * nbq + rows[3 * r + 2] / BLK) * D : NULL,
                     block_mask ? block_mask + (bh * nbq + rows[3 * r + 2] / BLK) * nbk : NULL,
                     sc, p, out + r * D,
                     m_out ? m_out + r : NULL, l_out ? l_out + r : NULL,
@@ -406,12 +436,13 @@ void orc_attention_rows(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
 }
 
 /* Every row; out is BSHD [B][Nq][H][128] BF16; lse [B][H][Nq] or NULL
- * (then k_mean may be NULL too). */
+ * (then k_mean may be NULL too); q_mean as in orc_attention_rows. */
 void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                    const float* q_scale, const float* k_scale, const float* v_scale,
-                   const float* k_mean,
+                   const float* k_mean, const float* q_mean,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
                    uint16_t* out, double* lse) {
+  const int64_t nbq = nblocks(Nq);
   #pragma omp parallel
   {
     double* sc = (double*)malloc(sizeof(double) * (size_t)Nkv);
@@ -421,7 +452,8 @@ void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
       for (int64_t h = 0; h < H; h++)
         for (int64_t i = 0; i < Nq; i++)
           attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
-                        b, h, i, lse ? k_mean + (b * H + h) * D : NULL, NULL, sc, p,
+                        b, h, i, lse ? k_mean + (b * H + h) * D : NULL,
+                        q_mean ? q_mean + ((b * H + h) * nbq + i / BLK) * D : NULL, NULL, sc, p,
                         out + ((b * Nq + i) * H + h) * D, NULL, NULL,
                         lse ? lse + (b * H + h) * Nq + i : NULL);
     free(sc);
@@ -433,11 +465,12 @@ void orc_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
  * Block-sparse attention: query i attends key j iff
  * block_mask[b][h][i / 128][j / 128] != 0 (mask [B][H][nbq][nbk] uint8).
  * Every row as in orc_attention over its allowed keys; rows without one get
- * output 0 and lse -inf.  lse and k_mean may be NULL together.
+ * output 0 and lse -inf.  lse and k_mean may be NULL together; q_mean as in
+ * orc_attention_rows.
  */
 void orc_attention_sparse(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                           const float* q_scale, const float* k_scale, const float* v_scale,
-                          const float* k_mean, const uint8_t* block_mask,
+                          const float* k_mean, const float* q_mean, const uint8_t* block_mask,
                           int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int fmt, float softmax_scale,
                           uint16_t* out, double* lse) {
   const int64_t nbq = nblocks(Nq), nbk = nblocks(Nkv);
@@ -451,6 +484,7 @@ void orc_attention_sparse(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
         for (int64_t i = 0; i < Nq; i++)
           attention_row(q8, k8, v8, q_scale, k_scale, v_scale, H, Nq, Nkv, fmt, softmax_scale,
                         b, h, i, lse ? k_mean + (b * H + h) * D : NULL,
+                        q_mean ? q_mean + ((b * H + h) * nbq + i / BLK) * D : NULL,
                         block_mask + ((b * H + h) * nbq + i / BLK) * nbk, sc, p,
                         out + ((b * Nq + i) * H + h) * D, NULL, NULL,
                         lse ? lse + (b * H + h) * Nq + i : NULL);
