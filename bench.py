@@ -94,12 +94,12 @@ def copy_calibration(torch, dev):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, q, k, v, rows_per_head, qk_format, block_mask=None):
+def cpu_baseline(cfg, q, k, v, rows_per_head, qk_format, block_mask=None, q_smooth=False):
     import numpy as np
 
     import oracle
     t0 = time.time()
-    codes = oracle.quantize(q, k, v, qk_format=qk_format)
+    codes = oracle.quantize(q, k, v, qk_format=qk_format, q_smooth=q_smooth)
     t_quant = time.time() - t0
     stride = max(1, cfg.Nq // rows_per_head)
     rows = np.array([[b, h, i] for b in range(cfg.B) for h in range(cfg.H)
@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0,
                     help="split-KV key ranges: 0 = the library's choice, 1 = none")
     ap.add_argument("--lse", action="store_true", help="also write the per-row LSE")
+    ap.add_argument("--q-smooth", action="store_true",
+                    help="Q smoothing per 128-token block with the Delta-S correction")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -152,7 +154,8 @@ def main():
     q, k, v = testkit.make_inputs(cfg)
     to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
-    pbytes, wbytes = sattn.packed_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv)
+    pbytes, wbytes = sattn.packed_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, qk_format=args.qk_format,
+                                        q_smooth=args.q_smooth)
     packed = torch.empty(pbytes, dtype=torch.uint8, device=dev)
     work = torch.empty(wbytes, dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.B, cfg.Nq, cfg.H, 128), dtype=torch.bfloat16, device=dev)
@@ -166,7 +169,8 @@ def main():
                           device=dev) if sparse else None
 
     def step():
-        p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work, qk_format=args.qk_format)
+        p = sattn.quantize_qkv(qd, kd, vd, packed=packed, workspace=work, qk_format=args.qk_format,
+                               q_smooth=args.q_smooth)
         ev[1].record()
         if sparse:
             # the block table is rebuilt every step, as for a mask predicted per step
@@ -216,7 +220,7 @@ def main():
         "dtype": "int8/fp8" if args.qk_format == "int8" else "fp8",
         "data": "synthetic",
         "config": dict(cfg.describe(), workload=cfg.name, softmax_scale=cfg.softmax_scale,
-                       qk_format=args.qk_format, kv_splits=splits, lse=args.lse,
+                       qk_format=args.qk_format, q_smooth=args.q_smooth, kv_splits=splits, lse=args.lse,
                        step="sattn_quantize_qkv + " + ("sattn_block_lut + sattn_fwd_sparse" if sparse else
                                                        "sattn_fwd" if cfg.Nq == cfg.Nkv else "sattn_fwd_cross")),
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
@@ -235,7 +239,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_rows_per_head, args.qk_format, mask_np)
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_rows_per_head, args.qk_format, mask_np,
+                                           args.q_smooth)
     print(json.dumps(rec), flush=True)
 
 

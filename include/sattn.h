@@ -85,6 +85,19 @@ typedef enum {
  */
 typedef enum { SATTN_QK_INT8 = 0, SATTN_QK_FP8 = 1 } sattn_qk_format;
 
+/*
+ * Option OR-ed into a qk_format: Q smoothing with the Delta-S correction
+ * (the MHA v4 page's import listing names a Q-smoothing kernel and a
+ * Delta-S kernel).  Per (b, h, 128-token Q block) the FP32 mean of the
+ * block's tokens (token order, one division by their count) is subtracted
+ * before the block is coded, and every score gets back Delta-S = ks(j) *
+ * (q_mean . kcode_j) * softmax_scale.  The packed buffer then also holds the
+ * means and a Delta-S table of B*H*ceil(Nq/128)*ceil(Nkv/128)*128 floats
+ * (size from sattn_packed_bytes_ex); the quantize call runs two more kernels
+ * and the forward one more addition per score.  Not with sattn_fwd_sparse.
+ */
+#define SATTN_QK_SMOOTH_Q 0x10
+
 /* ABI version of the loaded library (SATTN_ABI_VERSION). */
 int sattn_abi_version(void);
 
@@ -102,6 +115,9 @@ const char* sattn_status_string(sattn_status s);
  */
 sattn_status sattn_packed_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
                                 size_t* packed_bytes, size_t* workspace_bytes);
+/* The same for a qk_format (a format, optionally | SATTN_QK_SMOOTH_Q). */
+sattn_status sattn_packed_bytes_ex(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int qk_format,
+                                   size_t* packed_bytes, size_t* workspace_bytes);
 
 /*
  * Preprocessing: quantize BF16 q [B,Nq,H,128], k and v [B,Nkv,H,128] into
@@ -142,7 +158,8 @@ sattn_status sattn_fwd_cross(const void* packed, size_t packed_bytes,
  * The same three calls with the Q/K code format as an argument, and for the
  * forward calls an optional LSE output and split-KV.
  *
- * qk_format: a sattn_qk_format; another value is SATTN_ERR_INVALID_ARGUMENT.
+ * qk_format: a sattn_qk_format, optionally | SATTN_QK_SMOOTH_Q; another value
+ *   is SATTN_ERR_INVALID_ARGUMENT.
  *   The packed layout and its size are the same for both formats; a packed
  *   buffer must be read with the format it was written with (the library
  *   cannot tell them apart).
@@ -222,6 +239,13 @@ sattn_status sattn_fwd_sparse(const void* packed, size_t packed_bytes, int qk_fo
                               int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
                               float softmax_scale, const void* lut, size_t lut_bytes,
                               void* out, const int64_t* out_strides, float* lse, void* stream);
+
+/*
+ * Host-only: the Q block means [B][H][ceil(Nq/128)][128] FP32 of a host copy
+ * of a packed buffer quantized with SATTN_QK_SMOOTH_Q.
+ */
+sattn_status sattn_unpack_q_mean_host(const void* packed_host, size_t packed_bytes, int64_t B, int64_t H,
+                                      int64_t Nq, int64_t Nkv, int64_t D, float* q_mean);
 
 /*
  * Host-only inspection of a packed buffer (a host copy of it): writes the

@@ -23,7 +23,8 @@ unless one is passed).
 
 ``qk_format`` is "int8" (INT8 Q/K codes, scale amax/127: the gfx1201 backend
 page's INT8/FP8/BF16 path) or "fp8" (E4M3 Q/K codes, scale amax/448: the
-FP8/FP8/BF16 row of the MHA v4 page's MI355X table).  A Packed buffer records
+FP8/FP8/BF16 row of the MHA v4 page's MI355X table); ``q_smooth=True`` adds
+Q smoothing per 128-token block with the Delta-S correction.  A Packed buffer records
 its format and the forward calls pass it on (the ``_ex`` C entry points).
 
 As the gfx1201 backend page specifies its backend ("[ROCm] Add
@@ -59,6 +60,7 @@ SATTN_ERR_DEVICE = 4
 SATTN_ERR_LAUNCH = 5
 HEAD_DIM = 128
 QK_FORMATS = {"int8": 0, "fp8": 1}  # sattn_qk_format
+QK_SMOOTH_Q = 0x10                  # SATTN_QK_SMOOTH_Q
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -85,6 +87,8 @@ def _load():
         lib.sattn_status_string.argtypes = [ctypes.c_int]
         lib.sattn_status_string.restype = ctypes.c_char_p
         lib.sattn_packed_bytes.argtypes = [_I64] * 5 + [ctypes.POINTER(_SZ)] * 2
+        lib.sattn_packed_bytes_ex.argtypes = [_I64] * 5 + [ctypes.c_int] + [ctypes.POINTER(_SZ)] * 2
+        lib.sattn_unpack_q_mean_host.argtypes = [_P, _SZ] + [_I64] * 5 + [_P]
         lib.sattn_quantize_qkv.argtypes = [_P, _P, _P] + [_I64] * 5 + [_I64P] * 3 + [_P, _SZ, _P, _SZ, _P]
         lib.sattn_fwd.argtypes = [_P, _SZ] + [_I64] * 4 + [ctypes.c_float, _P, _I64P, _P]
         lib.sattn_fwd_cross.argtypes = [_P, _SZ] + [_I64] * 5 + [ctypes.c_float, _P, _I64P, _P]
@@ -102,7 +106,8 @@ def _load():
                                          + [ctypes.c_float, _P, _SZ, _P, _I64P, _P, _P])
         lib.sattn_unpack_host.argtypes = [_P, _SZ] + [_I64] * 5 + [_P] * 7
         lib.sattn_e4m3_encode.argtypes = [_P, _P, _I64, _P]
-        for f in ("sattn_packed_bytes", "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_cross",
+        for f in ("sattn_packed_bytes", "sattn_packed_bytes_ex", "sattn_unpack_q_mean_host",
+                  "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_cross",
                   "sattn_quantize_qkv_ex", "sattn_fwd_ex", "sattn_fwd_cross_ex", "sattn_fwd_workspace_bytes",
                   "sattn_block_lut_bytes", "sattn_block_lut", "sattn_fwd_sparse",
                   "sattn_unpack_host", "sattn_e4m3_encode"):
@@ -126,11 +131,13 @@ def abi_version() -> int:
     return int(_load().sattn_abi_version())
 
 
-def packed_bytes(B: int, H: int, Nq: int, Nkv: int, D: int = HEAD_DIM) -> Tuple[int, int]:
-    """(packed bytes, workspace bytes) for a problem."""
+def packed_bytes(B: int, H: int, Nq: int, Nkv: int, D: int = HEAD_DIM, qk_format: str = "int8",
+                 q_smooth: bool = False) -> Tuple[int, int]:
+    """(packed bytes, workspace bytes) for a problem (Q smoothing adds the
+    block means and the Delta-S table)."""
     pb, wb = _SZ(0), _SZ(0)
-    _check(_load().sattn_packed_bytes(B, H, Nq, Nkv, D, ctypes.byref(pb), ctypes.byref(wb)),
-           "sattn_packed_bytes")
+    _check(_load().sattn_packed_bytes_ex(B, H, Nq, Nkv, D, _format(qk_format, q_smooth), ctypes.byref(pb),
+                                         ctypes.byref(wb)), "sattn_packed_bytes")
     return int(pb.value), int(wb.value)
 
 
@@ -144,6 +151,7 @@ class Packed:
     Nkv: int
     squeeze_batch: bool = False
     qk_format: str = "int8"
+    q_smooth: bool = False
 
 
 def _stream_ptr(device: torch.device) -> int:
@@ -172,18 +180,19 @@ def _strides(x: torch.Tensor):
     return (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
 
 
-def _format(qk_format: str) -> int:
+def _format(qk_format: str, q_smooth: bool = False) -> int:
     if qk_format not in QK_FORMATS:
         raise ValueError(f"qk_format must be one of {sorted(QK_FORMATS)}, got {qk_format!r}")
-    return QK_FORMATS[qk_format]
+    return QK_FORMATS[qk_format] | (QK_SMOOTH_Q if q_smooth else 0)
 
 
 def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  packed: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, qk_format: str = "int8") -> Packed:
+                 workspace: Optional[torch.Tensor] = None, qk_format: str = "int8",
+                 q_smooth: bool = False) -> Packed:
     """BF16 q [B,Nq,H,128], k/v [B,Nkv,H,128] -> packed Q/K codes (INT8 or
     E4M3, per ``qk_format``), E4M3 V codes and scales."""
-    fmt = _format(qk_format)
+    fmt = _format(qk_format, q_smooth)
     q4, sq = _as4d(q, "q")
     k4, _ = _as4d(k, "k")
     v4, _ = _as4d(v, "v")
@@ -193,7 +202,7 @@ def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError(f"shape mismatch: q {tuple(q4.shape)} k {tuple(k4.shape)} v {tuple(v4.shape)}")
     if not (q4.device == k4.device == v4.device):
         raise ValueError("q, k, v must be on one device")
-    pb, wb = packed_bytes(B, H, Nq, Nkv, D)
+    pb, wb = packed_bytes(B, H, Nq, Nkv, D, qk_format, q_smooth)
     if packed is None:
         packed = torch.empty(pb, dtype=torch.uint8, device=q4.device)
     if workspace is None:
@@ -204,7 +213,7 @@ def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                          packed.numel() * packed.element_size(), workspace.data_ptr(),
                                          workspace.numel() * workspace.element_size(),
                                          _stream_ptr(q4.device)), "sattn_quantize_qkv")
-    return Packed(packed, B, H, Nq, Nkv, sq, qk_format)
+    return Packed(packed, B, H, Nq, Nkv, sq, qk_format, q_smooth)
 
 
 def _scale(softmax_scale: Optional[float]) -> float:
@@ -243,10 +252,10 @@ def _forward(name: str, packed: Packed, softmax_scale, out, return_lse: bool, nu
               int(num_splits), wptr, wlen, _stream_ptr(dev))
     lib = _load()
     if name == "sattn_fwd":
-        st = lib.sattn_fwd_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+        st = lib.sattn_fwd_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format, packed.q_smooth),
                               packed.B, packed.H, packed.Nq, HEAD_DIM, *common)
     else:
-        st = lib.sattn_fwd_cross_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+        st = lib.sattn_fwd_cross_ex(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format, packed.q_smooth),
                                     packed.B, packed.H, packed.Nq, packed.Nkv, HEAD_DIM, *common)
     _check(st, name)
     if not return_lse:
@@ -315,7 +324,7 @@ def fwd_sparse(packed: Packed, lut: BlockLut, softmax_scale: Optional[float] = N
     res, o4 = _out(packed, out)
     dev = o4.device
     lse = torch.empty((packed.B, packed.H, packed.Nq), dtype=torch.float32, device=dev) if return_lse else None
-    _check(_load().sattn_fwd_sparse(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format),
+    _check(_load().sattn_fwd_sparse(packed.buf.data_ptr(), packed.buf.numel(), _format(packed.qk_format, packed.q_smooth),
                                     packed.B, packed.H, packed.Nq, packed.Nkv, HEAD_DIM, _scale(softmax_scale),
                                     lut.buf.data_ptr(), lut.buf.numel(), o4.data_ptr(), _strides(o4),
                                     None if lse is None else lse.data_ptr(), _stream_ptr(dev)), "sattn_fwd_sparse")
@@ -328,7 +337,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
               causal: bool = False, attn_mask: Optional[torch.Tensor] = None,
               dropout_p: float = 0.0, cu_seqlens: Optional[torch.Tensor] = None,
-              qk_format: str = "int8", return_lse: bool = False, num_splits: int = 1):
+              qk_format: str = "int8", return_lse: bool = False, num_splits: int = 1,
+              q_smooth: bool = False):
     """Quantize and attend.  Rejects what this path does not compute."""
     if causal:
         raise NotImplementedError("causal attention is not supported")
@@ -338,7 +348,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise NotImplementedError("dropout is not supported")
     if cu_seqlens is not None:
         raise NotImplementedError("packed multi-sequence (cu_seqlens) inputs are not supported")
-    p = quantize_qkv(q, k, v, qk_format=qk_format)
+    p = quantize_qkv(q, k, v, qk_format=qk_format, q_smooth=q_smooth)
     if p.Nq == p.Nkv:
         return fwd(p, softmax_scale, out, return_lse=return_lse, num_splits=num_splits)
     return fwd_cross(p, softmax_scale, out, return_lse=return_lse, num_splits=num_splits)
@@ -364,6 +374,10 @@ def unpack_host(packed: Packed) -> Dict[str, "object"]:
                                                                   "k_scale", "v_scale", "k_mean"))),
            "sattn_unpack_host")
     r["qk_format"] = packed.qk_format
+    if packed.q_smooth:
+        r["q_mean"] = np.empty((B, H, nbq, HEAD_DIM), np.float32)
+        _check(_load().sattn_unpack_q_mean_host(host.ctypes.data, host.size, B, H, Nq, Nkv, HEAD_DIM,
+                                                r["q_mean"].ctypes.data), "sattn_unpack_q_mean_host")
     return r
 
 

@@ -80,7 +80,21 @@ sattn_status check_device() {
 
 sattn_status launch_status(hipError_t e) { return e == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH; }
 
-bool valid_format(int f) { return f == SATTN_QK_INT8 || f == SATTN_QK_FP8; }
+// qk_format: a sattn_qk_format, optionally OR-ed with SATTN_QK_SMOOTH_Q.
+bool valid_format(int f) {
+  const int base = f & ~SATTN_QK_SMOOTH_Q;
+  return base == SATTN_QK_INT8 || base == SATTN_QK_FP8;
+}
+bool is_fp8(int f) { return (f & ~SATTN_QK_SMOOTH_Q) == SATTN_QK_FP8; }
+bool is_qsmooth(int f) { return (f & SATTN_QK_SMOOTH_Q) != 0; }
+
+// Q smoothing adds a Delta-S table of B*H*nbq*nbk*128 floats; past 2^40
+// bytes (far beyond device memory) the sizes are refused.
+sattn_status check_qsmooth(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int f) {
+  if (!is_qsmooth(f)) return SATTN_OK;
+  const double bytes = (double)B * (double)H * (double)sattn::nblocks(Nq) * (double)sattn::nblocks(Nkv) * 512.0;
+  return bytes > 1099511627776.0 ? SATTN_ERR_UNSUPPORTED : SATTN_OK;
+}
 
 // Split-KV: how many key-tile ranges, and tiles per range, for a request of
 // num_splits (0: automatic).  The automatic choice splits only a launch whose
@@ -119,6 +133,8 @@ sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, 
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
   if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
+  if ((s = check_qsmooth(B, H, Nq, Nkv, qk_format)) != SATTN_OK) return s;
+  if (lut != nullptr && is_qsmooth(qk_format)) return SATTN_ERR_UNSUPPORTED;
   if (num_splits < 0 || num_splits > SATTN_MAX_SPLITS) return SATTN_ERR_INVALID_ARGUMENT;
   if (packed == nullptr || out == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(packed) || !aligned16(out)) return SATTN_ERR_INVALID_ARGUMENT;
@@ -139,14 +155,14 @@ sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, 
   sattn::AttnArgs a;
   s = get_strides(out_strides, Nq, H, a.o_str);
   if (s != SATTN_OK) return s;
-  a.L = sattn::make_layout(B, H, Nq, Nkv);
+  a.L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format));
   if (packed_bytes < a.L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
   s = check_device();
   if (s != SATTN_OK) return s;
   a.packed = static_cast<const uint8_t*>(packed);
   a.softmax_scale = softmax_scale;
   a.out = static_cast<uint16_t*>(out);
-  a.fp8qk = qk_format == SATTN_QK_FP8;
+  a.fp8qk = is_fp8(qk_format);
   a.lse = lse;
   a.splits = sp.splits;
   a.tps = sp.tps;
@@ -180,14 +196,21 @@ const char* sattn_status_string(sattn_status s) {
   return "unknown status";
 }
 
-sattn_status sattn_packed_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
-                                size_t* packed_bytes, size_t* workspace_bytes) {
+sattn_status sattn_packed_bytes_ex(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, int qk_format,
+                                   size_t* packed_bytes, size_t* workspace_bytes) {
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
-  const Layout L = sattn::make_layout(B, H, Nq, Nkv);
+  if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
+  if ((s = check_qsmooth(B, H, Nq, Nkv, qk_format)) != SATTN_OK) return s;
+  const Layout L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format));
   if (packed_bytes) *packed_bytes = L.packed_bytes;
   if (workspace_bytes) *workspace_bytes = L.workspace_bytes;
   return SATTN_OK;
+}
+
+sattn_status sattn_packed_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                size_t* packed_bytes, size_t* workspace_bytes) {
+  return sattn_packed_bytes_ex(B, H, Nq, Nkv, D, SATTN_QK_INT8, packed_bytes, workspace_bytes);
 }
 
 sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
@@ -199,6 +222,7 @@ sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
   if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
+  if ((s = check_qsmooth(B, H, Nq, Nkv, qk_format)) != SATTN_OK) return s;
   if (!q || !k || !v || !packed || !workspace) return SATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(packed) || !aligned16(workspace))
     return SATTN_ERR_INVALID_ARGUMENT;
@@ -206,7 +230,7 @@ sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
   if ((s = get_strides(q_strides, Nq, H, a.q_str)) != SATTN_OK) return s;
   if ((s = get_strides(k_strides, Nkv, H, a.k_str)) != SATTN_OK) return s;
   if ((s = get_strides(v_strides, Nkv, H, a.v_str)) != SATTN_OK) return s;
-  a.L = sattn::make_layout(B, H, Nq, Nkv);
+  a.L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format));
   if (packed_bytes < a.L.packed_bytes || workspace_bytes < a.L.workspace_bytes)
     return SATTN_ERR_BUFFER_TOO_SMALL;
   s = check_device();
@@ -216,7 +240,7 @@ sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
   a.v = static_cast<const uint16_t*>(v);
   a.packed = static_cast<uint8_t*>(packed);
   a.workspace = static_cast<uint8_t*>(workspace);
-  a.fp8qk = qk_format == SATTN_QK_FP8;
+  a.fp8qk = is_fp8(qk_format);
   return launch_status(sattn::launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -337,6 +361,18 @@ sattn_status sattn_unpack_host(const void* packed_host, size_t packed_bytes, int
   if (k_scale) memcpy(k_scale, P + L.off_ks, (size_t)BH * L.nbk * 4);
   if (v_scale) memcpy(v_scale, P + L.off_vs, (size_t)BH * 128 * 4);
   if (k_mean) memcpy(k_mean, P + L.off_km, (size_t)BH * 128 * 4);
+  return SATTN_OK;
+}
+
+sattn_status sattn_unpack_q_mean_host(const void* packed_host, size_t packed_bytes, int64_t B, int64_t H,
+                                      int64_t Nq, int64_t Nkv, int64_t D, float* q_mean) {
+  sattn_status s = check_dims(B, H, Nq, Nkv, D);
+  if (s != SATTN_OK) return s;
+  if ((s = check_qsmooth(B, H, Nq, Nkv, SATTN_QK_SMOOTH_Q)) != SATTN_OK) return s;
+  if (packed_host == nullptr || q_mean == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
+  const Layout L = sattn::make_layout(B, H, Nq, Nkv, true);
+  if (packed_bytes < L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
+  memcpy(q_mean, static_cast<const uint8_t*>(packed_host) + L.off_qm, (size_t)(B * H * L.nbq) * 128 * 4);
   return SATTN_OK;
 }
 

@@ -75,6 +75,8 @@ struct AttnP {
   float* lpart;  //   and their LSE [splits][B*H][Nq]
   const int32_t* lut_counts;    // block-sparse: key tiles per query tile [B*H*mt]
   const uint32_t* lut_entries;  //   and their entries [B*H*mt][nbk]
+  const float* ds;              // Q smoothing: Delta-S [B*H][nbq][nbk*128]
+  const float* qm;              //   and the Q block means [B*H][nbq][128]
   int64_t G;     // logical workgroups: B*H*splits*mt
   int64_t BH;
   int H, Nq, Nkv, nbq, nbk, mt;
@@ -139,9 +141,13 @@ constexpr float kMagicF = 12582912.0f;
 // FP8QK: Q and K codes are E4M3 (the FP8/FP8/BF16 format): S^T comes from
 // v_mfma_scale_f32_32x32x64_f8f6f4 in FP32, the K operands being the same
 // LDS reads taken two 16-byte chunks per MFMA.
-template <bool FP8QK, bool SPARSE>
+// QSMOOTH: Q was smoothed per block; each score gets the Delta-S term of its
+// query block and key, staged with the tile (1 KiB: the two query blocks'
+// 128 values) in LDS.
+template <bool FP8QK, bool SPARSE, bool QSMOOTH>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int kStage = kStageBytes + (QSMOOTH ? 1024 : 0);
   constexpr int NW = 8;
   constexpr int BM = NW * 32;
 
@@ -229,7 +235,16 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     const int64_t tile = tile_of(t);
     const uint8_t* src = (c0 < 1024 ? kbase + tile * kTileBytes + c0 * 16
                                     : vbase + tile * kTileBytes + (c0 - 1024) * 16) + lane * 16;
-    uint8_t* dst = smem + stage * kStageBytes + c0 * 16;
+    uint8_t* dst = smem + stage * kStage + c0 * 16;
+    if constexpr (QSMOOTH) {
+      // the first copying wave also brings the tile's Delta-S: lanes 0-31
+      // the first query block's 128 values, lanes 32-63 the second's
+      if (widx == 0) {
+        const int qb = min(2 * mtile + (lane >> 5), p.nbq - 1);
+        const float* dsrc = p.ds + ((bh * p.nbq + qb) * (int64_t)p.nbk + t0 + tile) * 128 + (lane & 31) * 4;
+        copy_to_lds_off<0>(reinterpret_cast<const uint8_t*>(dsrc), smem + stage * kStage + 2 * kTileBytes);
+      }
+    }
     for (int i = 0; i < per / 256; ++i) {
       copy_to_lds_off<0>(src + i * 4096, dst + i * 4096);
       copy_to_lds_off<1024>(src + i * 4096, dst + i * 4096);
@@ -252,6 +267,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   float c_cur = 0.0f;       // dequant scale of the tile whose S is held
   bool masked_cur = false;  // block-sparse: that tile is masked for this group
   bool pv_skip = false;     // block-sparse: the P registers belong to a masked tile
+  int dstage_cur = 0;       // Q smoothing: the LDS stage holding that tile's Delta-S
   // The K block scales are read through the constant address space, which
   // makes these uniform loads scalar (s_load, counted by lgkmcnt).  A vector
   // load here would be followed by a vmcnt wait that also waits for the
@@ -276,7 +292,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     __builtin_amdgcn_s_setprio(2);
     if (isA && t >= 1 && t + 1 < nbk) copy_tile(t + 1, kst == 2 ? 0 : kst + 1, w, 4);
     if (do_pv && !(SPARSE && pv_skip)) {
-      const uint8_t* Vs = smem + (kst == 0 ? 2 : kst - 1) * kStageBytes + kTileBytes;  // stage of t-1
+      const uint8_t* Vs = smem + (kst == 0 ? 2 : kst - 1) * kStage + kTileBytes;  // stage of t-1
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const v8i Bp = {(int)P[g][0], (int)P[g][1], (int)P[g][2], (int)P[g][3],
@@ -304,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       if (do_s) masked_cur = mask_all;
     }
     if (do_s && !(SPARSE && mask_all)) {
-      const uint8_t* Ks = smem + kst * kStageBytes;
+      const uint8_t* Ks = smem + kst * kStage;
       v4i kf[4][4];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -351,7 +367,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      c_cur = qscale * ksc4[tile_of(t)] * p.sl2e;
+      // (Q smoothing: a block with qs = 0 has all-zero codes; its scores are
+      // the Delta-S table's values, held in units of 2^-20 * ks)
+      c_cur = (QSMOOTH && qscale == 0.0f ? 0x1p-20f : qscale) * ksc4[tile_of(t)] * p.sl2e;
+      if constexpr (QSMOOTH) dstage_cur = kst;
       if (mask_rem < 128) {
         // the first masked key offset of this lane half; the empty asm before
         // each comparison keeps the 64 lane masks from all being computed up
@@ -381,7 +400,30 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     // below their rounding unit) and keeps -inf at -inf.
     const float c = c_cur == 0.0f ? 1.17549435e-38f : c_cur;
     float mt;
-    if constexpr (FP8QK) {
+    if constexpr (QSMOOTH) {
+      // add Delta-S (in the units of S: the table holds (qmean . kcode) / qs)
+      // of this group's query block to every score, written back over S,
+      // then the row maximum on floats; masked keys stay -inf
+      const float* dsl = reinterpret_cast<const float*>(smem + dstage_cur * kStage + 2 * kTileBytes) +
+                         (isA ? 0 : 128) + 4 * hh;
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float4 d4 = *reinterpret_cast<const float4*>(dsl + 32 * kb + 8 * a);
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int b2 = 0; b2 < 4; ++b2) {
+            const int r = 4 * a + b2;
+            const float tt = __int_as_float(S[kb][r]) + dv[b2];
+            S[kb][r] = __float_as_int(tt);
+            mx = fmaxf(mx, tt);
+          }
+        }
+      mx = fmaxf(mx, other_half_f(mx));
+      mt = FP8QK ? mx * c : (mx - kMagicF) * c;
+    } else if constexpr (FP8QK) {
       // FP32 scores (unscaled); masked keys are -inf
       float mx = -__builtin_inff();
 #pragma unroll
@@ -428,8 +470,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float sf = __int_as_float(S[kb][r0 + i]);
-          pv[i] = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(FP8QK || kFoldBias ? sf : sf - kMagicF, c, nb));
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(FP8QK || kFoldBias ? sf : sf - kMagicF, c, nb));
           // the first term starts the sum (p >= 0, so 0 + p == p)
           ls[i] = (g == 0 && j == 0) ? pv[i] : ls[i] + pv[i];
         }
@@ -530,8 +571,16 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qc[e], kmr[16 * m + 4 * j + e], acc);
       }
+    float accm = 0.0f;
+    if constexpr (QSMOOTH) {
+      // plus the Q block mean against the K mean
+      const float* qmr = p.qm + (bh * p.nbq + min(qblk, p.nbq - 1)) * 128 + 64 * hh;
+#pragma unroll
+      for (int d = 0; d < 64; ++d) accm = __builtin_fmaf(qmr[d], kmr[d], accm);
+    }
     acc += other_half_f(acc);
-    shift = p.scale * qscale * acc;
+    accm += other_half_f(accm);
+    shift = p.scale * (qscale * acc + accm);
   }
   if (q < p.Nq) {
     // (block-sparse: a row whose query block attends none of the listed
@@ -650,11 +699,11 @@ __global__ __launch_bounds__(256) void k_block_lut(LutP p) {
   if (lane == 0) p.counts[g] = count;
 }
 
-template <bool FP8QK, bool SPARSE>
+template <bool FP8QK, bool SPARSE, bool QSMOOTH>
 hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
   constexpr int BM = 256;
-  constexpr int kLds = 3 * kStageBytes;
+  constexpr int kLds = 3 * (kStageBytes + (QSMOOTH ? 1024 : 0));
   // Raising the dynamic LDS limit is per function and device, once each
   // (a repeated call from a racing thread is harmless).
   constexpr int kMaxDev = 64;
@@ -663,7 +712,7 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDev || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<FP8QK, SPARSE>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<FP8QK, SPARSE, QSMOOTH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDev) attr_set[dev] = true;
@@ -699,7 +748,9 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const int64_t G8 = (p.G + 7) / 8 * 8;
   p.lut_counts = a.lut_counts;
   p.lut_entries = a.lut_entries;
-  hipLaunchKernelGGL((attn_pp_kernel<FP8QK, SPARSE>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
+  p.ds = QSMOOTH ? reinterpret_cast<const float*>(a.packed + L.off_ds) : nullptr;
+  p.qm = QSMOOTH ? reinterpret_cast<const float*>(a.packed + L.off_qm) : nullptr;
+  hipLaunchKernelGGL((attn_pp_kernel<FP8QK, SPARSE, QSMOOTH>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   CombP c{p.opart, p.lpart, p.out, p.lse, p.os0, p.os1, p.os2, p.BH * L.Nq, p.H, p.Nq, p.splits};
@@ -712,8 +763,10 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
   (void)cross;
   if (a.lut_counts != nullptr)
-    return a.fp8qk ? launch_pp<true, true>(a, stream) : launch_pp<false, true>(a, stream);
-  return a.fp8qk ? launch_pp<true, false>(a, stream) : launch_pp<false, false>(a, stream);
+    return a.fp8qk ? launch_pp<true, true, false>(a, stream) : launch_pp<false, true, false>(a, stream);
+  if (a.L.qsmooth)
+    return a.fp8qk ? launch_pp<true, false, true>(a, stream) : launch_pp<false, false, true>(a, stream);
+  return a.fp8qk ? launch_pp<true, false, false>(a, stream) : launch_pp<false, false, false>(a, stream);
 }
 
 hipError_t launch_block_lut(const uint8_t* mask, const Layout& L, uint8_t* lut, hipStream_t stream) {

@@ -23,6 +23,12 @@
 //        Columns of keys past Nkv are zero.
 //   q_scale [B][H][nbq], k_scale [B][H][nbk], v_scale [B][H][128],
 //   k_mean  [B][H][128]  (FP32)
+//   with Q smoothing only:
+//   q_mean  [B][H][nbq][128]  FP32 block means of Q
+//   d_s     [B][H][nbq][nbk * 128]  FP32 Delta-S: for query block i and key
+//           j, (q_mean[i] . kcode[j]) / u_i with u_i = qs_i (2^-20 if qs_i = 0),
+//           in the units of the Q.K^T accumulator of block i; entries of keys
+//           past Nkv are zero.
 //
 // Workspace: k_part [B][H][nbk][128] FP32 block sums of K and v_part
 // [B][H][nbk][128] FP32 block maxima of |V|.
@@ -47,14 +53,17 @@ SATTN_HD inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int64_t B, H, Nq, Nkv, nbq, nbk;
-  size_t off_q8, off_k8, off_v8, off_qs, off_ks, off_vs, off_km, packed_bytes;
+  bool qsmooth;
+  size_t off_q8, off_k8, off_v8, off_qs, off_ks, off_vs, off_km, off_qm, off_ds, packed_bytes;
   size_t ws_kpart, ws_vpart, workspace_bytes;
 };
 
-// Callers validate sizes first (no overflow for N <= 2^24, B*H <= 2^31).
-inline Layout make_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv) {
+// Callers validate sizes first (no overflow for N <= 2^24, B*H <= 2^31, and
+// for Q smoothing the Delta-S section below 2^40 bytes).
+inline Layout make_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, bool qsmooth = false) {
   Layout L;
   L.B = B; L.H = H; L.Nq = Nq; L.Nkv = Nkv;
+  L.qsmooth = qsmooth;
   L.nbq = nblocks(Nq);
   L.nbk = nblocks(Nkv);
   const size_t bh = (size_t)B * (size_t)H;
@@ -66,6 +75,11 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv) {
   L.off_ks = o; o = align256(o + bh * (size_t)L.nbk * 4);
   L.off_vs = o; o = align256(o + bh * kD * 4);
   L.off_km = o; o = align256(o + bh * kD * 4);
+  L.off_qm = L.off_ds = 0;
+  if (qsmooth) {
+    L.off_qm = o; o = align256(o + bh * (size_t)L.nbq * kD * 4);
+    L.off_ds = o; o = align256(o + bh * (size_t)L.nbq * (size_t)L.nbk * kBlk * 4);
+  }
   L.packed_bytes = o;
   size_t w = 0;
   L.ws_kpart = w; w = align256(w + bh * (size_t)L.nbk * kD * 4);

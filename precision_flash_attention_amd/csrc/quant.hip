@@ -21,6 +21,10 @@
 // x / s) and fall back to the exact division only when y lies so close to a
 // rounding boundary that the two could round differently.  Build with
 // -ffp-contract=off.
+//
+// With Q smoothing (the MHA v4 page's import listing: a Q-smoothing kernel
+// and a Delta-S kernel) two more steps run: the Q block means (before the
+// codes, which then quantize q - mean) and the Delta-S table (after them).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -111,6 +115,57 @@ __global__ __launch_bounds__(256) void k_stats(StatsP p) {
   ko[1] = make_float4(s[4], s[5], s[6], s[7]);
   vo[0] = make_float4(m[0], m[1], m[2], m[3]);
   vo[1] = make_float4(m[4], m[5], m[6], m[7]);
+}
+
+// Q smoothing: per (b, Q block t, head, 8-channel group) the FP32 sum of the
+// block's tokens in token order, divided once by the token count.
+struct QStatsP {
+  const uint16_t* q;
+  int64_t qs0, qs1, qs2;
+  int64_t B, H, Nq, nbq;
+  float* q_mean;
+};
+
+__global__ __launch_bounds__(256) void k_qstats(QStatsP p) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= p.B * p.nbq * p.H * 16) return;
+  const int g = (int)(tid & 15);
+  int64_t r = tid >> 4;
+  const int64_t h = r % p.H;
+  r /= p.H;
+  const int64_t t = r % p.nbq;
+  const int64_t b = r / p.nbq;
+  const int64_t n0 = t * kBlk;
+  const int64_t n1 = n0 + kBlk < p.Nq ? n0 + kBlk : p.Nq;
+  const uint16_t* qp = p.q + b * p.qs0 + h * p.qs2 + 8 * g;
+  float s[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s[c] = 0.0f;
+  int64_t n = n0;
+  for (; n + 8 <= n1; n += 8) {
+    uint4 qq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qq[i] = *reinterpret_cast<const uint4*>(qp + (n + i) * p.qs1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float qf[8];
+      unpack8(qq[i], qf);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[c] = s[c] + qf[c];
+    }
+  }
+  for (; n < n1; ++n) {
+    float qf[8];
+    unpack8(*reinterpret_cast<const uint4*>(qp + n * p.qs1), qf);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] = s[c] + qf[c];
+  }
+  const float cnt = (float)(n1 - n0);
+  float* o = p.q_mean + ((b * p.H + h) * p.nbq + t) * kD + 8 * g;
+  reinterpret_cast<float4*>(o)[0] = make_float4(__fdiv_rn(s[0], cnt), __fdiv_rn(s[1], cnt),
+                                                __fdiv_rn(s[2], cnt), __fdiv_rn(s[3], cnt));
+  reinterpret_cast<float4*>(o)[1] = make_float4(__fdiv_rn(s[4], cnt), __fdiv_rn(s[5], cnt),
+                                                __fdiv_rn(s[6], cnt), __fdiv_rn(s[7], cnt));
 }
 
 // ---------------------------------------------------------- 2. finalize ----
@@ -226,6 +281,7 @@ struct CodeP {
   float* k_scale;
   const float* v_scale;
   const float* k_mean;
+  const float* q_mean;  // Q smoothing: block means [BH][nbq][128], or null
 };
 
 // One workgroup of 256 threads per (tensor, b, h, 128-token block).  Thread
@@ -314,10 +370,13 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
 
   // ---- Q and K: block amax, scale amax/127 with INT8 codes, or amax/448
   // with E4M3 codes (the FP8 Q/K format).
-  if (kind == 1) {
+  // K: subtract the sequence mean; Q with smoothing: the block mean
+  const float* mrow = kind == 1 ? p.k_mean + bh * kD
+                    : p.q_mean != nullptr ? p.q_mean + (bh * p.nbq + t) * kD : nullptr;
+  if (mrow != nullptr) {
     float mean[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) mean[c] = p.k_mean[bh * kD + 8 * cg + c];
+    for (int c = 0; c < 8; ++c) mean[c] = mrow[8 * cg + c];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -354,6 +413,77 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
   }
 }
 
+// ------------------------------------------------------------ 4. Delta-S ----
+// D[bh][i][t*128 + j] = (q_mean[bh][i] . kcode(t, j)) / u_i for every Q block
+// i, u_i = qs_i (2^-20 when qs_i = 0, a block of equal tokens: its scores
+// are Delta-S alone, kept at FP32 resolution): the score term that restores the Q
+// block mean, in the units of the Q.K^T accumulator (times qs * ks it is the
+// score), so the attention kernel adds it to the accumulator as it is.  The
+// codes of keys past Nkv are zero, so their entries are too.  One workgroup of 128
+// threads per (b, h, key tile), a thread per key holding its 128 decoded
+// codes; the means pass through LDS 16 blocks at a time (every thread reads
+// the same address: a broadcast).
+struct DsP {
+  const uint8_t* k8;
+  const float* q_scale;
+  const float* q_mean;
+  float* ds;
+  int64_t nbq, nbk;
+  int fp8qk;
+};
+
+constexpr int kDsChunk = 16;
+
+template <bool FP8>
+__global__ __launch_bounds__(128) void k_delta_s(DsP p) {
+  __shared__ __attribute__((aligned(16))) float sq[kDsChunk][kD];
+  const int64_t g = blockIdx.x;  // bh * nbk + t
+  const int64_t bh = g / p.nbk, t = g % p.nbk;
+  const int j = threadIdx.x;
+  const uint8_t* row = p.k8 + g * kTileBytes + j * 128;
+  float kc[kD];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + (((cc ^ swz(j)) & 7) << 4));
+    const int w[4] = {(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (FP8) {
+        // E4M3 bytes -> values (exact in FP32)
+        kc[16 * cc + 4 * q + 0] = __builtin_amdgcn_cvt_f32_fp8(w[q], 0);
+        kc[16 * cc + 4 * q + 1] = __builtin_amdgcn_cvt_f32_fp8(w[q], 1);
+        kc[16 * cc + 4 * q + 2] = __builtin_amdgcn_cvt_f32_fp8(w[q], 2);
+        kc[16 * cc + 4 * q + 3] = __builtin_amdgcn_cvt_f32_fp8(w[q], 3);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kc[16 * cc + 4 * q + e] = (float)(int8_t)(w[q] >> (8 * e));
+      }
+    }
+  }
+  const float* qsr = p.q_scale + bh * p.nbq;
+  const float* qm = p.q_mean + bh * p.nbq * kD;
+  float* out = p.ds + bh * p.nbq * (p.nbk * kBlk) + t * kBlk + j;
+  for (int64_t i0 = 0; i0 < p.nbq; i0 += kDsChunk) {
+    const int n = (int)(p.nbq - i0 < kDsChunk ? p.nbq - i0 : kDsChunk);
+    __syncthreads();
+    for (int x = j; x < n * kD; x += 128) sq[x / kD][x % kD] = qm[(i0 + x / kD) * kD + x % kD];
+    __syncthreads();
+    for (int i = 0; i < n; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int d = 0; d < kD; d += 4) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&sq[i][d]);
+        acc = __builtin_fmaf(m4.x, kc[d], acc);
+        acc = __builtin_fmaf(m4.y, kc[d + 1], acc);
+        acc = __builtin_fmaf(m4.z, kc[d + 2], acc);
+        acc = __builtin_fmaf(m4.w, kc[d + 3], acc);
+      }
+      const float u = qsr[i0 + i];
+      out[(i0 + i) * (p.nbk * kBlk)] = u > 0.0f ? __fdiv_rn(acc, u) : acc * 0x1p20f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_e4m3(const float* x, uint8_t* out, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) out[i] = (uint8_t)e4m3_hw(clamp448(x[i]));
@@ -377,6 +507,14 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(k_stats, dim3((unsigned)((sthreads + 255) / 256)), dim3(256), 0, stream, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  float* q_mean = L.qsmooth ? reinterpret_cast<float*>(a.packed + L.off_qm) : nullptr;
+  if (L.qsmooth) {
+    QStatsP qp{a.q, a.q_str[0], a.q_str[1], a.q_str[2], L.B, L.H, L.Nq, L.nbq, q_mean};
+    const int64_t qthreads = L.B * L.nbq * L.H * 16;
+    hipLaunchKernelGGL(k_qstats, dim3((unsigned)((qthreads + 255) / 256)), dim3(256), 0, stream, qp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   FinP fp{kpart, vpart, BH, L.nbk, L.Nkv, k_mean, v_scale};
   hipLaunchKernelGGL(k_finalize, dim3((unsigned)BH, 4), dim3(256), 0, stream, fp);
@@ -388,8 +526,16 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
            a.v_str[0], a.v_str[1], a.v_str[2],
            L.H, L.Nq, L.Nkv, L.nbq, L.nbk, BH, a.fp8qk ? 1 : 0,
            a.packed + L.off_q8, a.packed + L.off_k8, a.packed + L.off_v8,
-           q_scale, k_scale, v_scale, k_mean};
+           q_scale, k_scale, v_scale, k_mean, q_mean};
   hipLaunchKernelGGL(k_codes, dim3((unsigned)(BH * (L.nbq + 2 * L.nbk))), dim3(256), 0, stream, cp);
+  e = hipGetLastError();
+  if (e != hipSuccess || !L.qsmooth) return e;
+  DsP dp{a.packed + L.off_k8, q_scale, q_mean, reinterpret_cast<float*>(a.packed + L.off_ds),
+         L.nbq, L.nbk, a.fp8qk ? 1 : 0};
+  if (a.fp8qk)
+    hipLaunchKernelGGL(k_delta_s<true>, dim3((unsigned)(BH * L.nbk)), dim3(128), 0, stream, dp);
+  else
+    hipLaunchKernelGGL(k_delta_s<false>, dim3((unsigned)(BH * L.nbk)), dim3(128), 0, stream, dp);
   return hipGetLastError();
 }
 

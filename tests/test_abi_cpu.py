@@ -320,3 +320,32 @@ def test_product_does_not_reference_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
                 assert "testkit" not in text, f
+
+
+def test_q_smoothing_sizes_and_flags(lib):
+    # the option adds the block means and the Delta-S table
+    B, H, Nq, Nkv = 2, 3, 300, 700
+    base = sattn.packed_bytes(B, H, Nq, Nkv)[0]
+    nbq, nbk = 3, 6
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = base + a(B * H * nbq * 128 * 4) + a(B * H * nbq * nbk * 128 * 4)
+    assert sattn.packed_bytes(B, H, Nq, Nkv, q_smooth=True)[0] == want
+    assert sattn.packed_bytes(B, H, Nq, Nkv, qk_format="fp8", q_smooth=True)[0] == want
+    pb = ctypes.c_size_t()
+    assert lib.sattn_packed_bytes_ex(1, 2, 256, 256, 128, 0x20, ctypes.byref(pb), None) == INVALID
+    assert lib.sattn_packed_bytes_ex(1, 2, 256, 256, 128, 0x12, ctypes.byref(pb), None) == INVALID
+    # Delta-S beyond 2^40 bytes is refused
+    assert lib.sattn_packed_bytes_ex(1, 1 << 8, 1 << 24, 1 << 17, 128, 0x10, ctypes.byref(pb), None) == UNSUPPORTED
+    st = strides(65536, 256, 128)
+    small = sattn.packed_bytes(1, 2, 256, 256)[0]   # enough without smoothing only
+    assert lib.sattn_quantize_qkv_ex(ALIGNED, ALIGNED, ALIGNED, 1, 2, 256, 256, 128, st, None, None, 0x10,
+                                     ALIGNED, small, ALIGNED, 1 << 40, None) == SMALL
+    assert lib.sattn_quantize_qkv_ex(ALIGNED, ALIGNED, ALIGNED, 1, 2, 256, 256, 128, st, None, None, 0x11,
+                                     ALIGNED, 1 << 40, ALIGNED, 1 << 40, None) == DEVICE
+    assert fwd_ex(lib, False, fmt=0x10, pbytes=sattn.packed_bytes(1, 2, 256, 256)[0]) == SMALL
+    assert fwd_ex(lib, False, fmt=0x11) == DEVICE
+    n = _lut_bytes(1, 2, 256, 256)
+    assert lib.sattn_fwd_sparse(ALIGNED, 1 << 40, 0x10, 1, 2, 256, 256, 128, ctypes.c_float(0.088), ALIGNED, n,
+                                ALIGNED, None, None, None) == UNSUPPORTED
+    assert lib.sattn_unpack_q_mean_host(None, 10, 1, 2, 256, 256, 128, ALIGNED) == INVALID
+    assert lib.sattn_unpack_q_mean_host(ALIGNED, 10, 1, 2, 256, 256, 128, ALIGNED) == SMALL
