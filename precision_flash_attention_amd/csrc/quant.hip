@@ -416,13 +416,19 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
 // ------------------------------------------------------------ 4. Delta-S ----
 // D[bh][i][t*128 + j] = (q_mean[bh][i] . kcode(t, j)) / u_i for every Q block
 // i, u_i = qs_i (2^-20 when qs_i = 0, a block of equal tokens: its scores
-// are Delta-S alone, kept at FP32 resolution): the score term that restores the Q
-// block mean, in the units of the Q.K^T accumulator (times qs * ks it is the
-// score), so the attention kernel adds it to the accumulator as it is.  The
-// codes of keys past Nkv are zero, so their entries are too.  One workgroup of 128
-// threads per (b, h, key tile), a thread per key holding its 128 decoded
-// codes; the means pass through LDS 16 blocks at a time (every thread reads
-// the same address: a broadcast).
+// are Delta-S alone, kept at FP32 resolution): the score term that restores
+// the Q block mean, in the units of the Q.K^T accumulator (times qs * ks it
+// is the score), so the attention kernel adds it to the accumulator as it
+// is.  The codes of keys past Nkv are zero, so their entries are too.
+//
+// Per (b, h) this is a [nbq x 128] x [128 x Nkv] FP32 product: it runs on
+// the FP32 MFMA (32x32x2), whose rate is twice that of FP32 FMAs on the
+// vector ALU.  The decoded codes are exact in FP32.  One workgroup of four
+// waves per (b, h, key tile); wave w holds the 32 keys 32w.. of the tile as
+// the B operand (64 registers: lane half h supplies channel 64h + s at step
+// s) and sweeps the Q blocks 32 at a time, the means of its 32 blocks times
+// 1 / u as the A operand (lane l: block l % 32, channels 64h .. 64h + 63),
+// loading the next group's means while the MFMAs of this one run.
 struct DsP {
   const uint8_t* k8;
   const float* q_scale;
@@ -432,55 +438,78 @@ struct DsP {
   int fp8qk;
 };
 
-constexpr int kDsChunk = 16;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <bool FP8>
-__global__ __launch_bounds__(128) void k_delta_s(DsP p) {
-  __shared__ __attribute__((aligned(16))) float sq[kDsChunk][kD];
+__global__ __launch_bounds__(256) void k_delta_s(DsP p) {
   const int64_t g = blockIdx.x;  // bh * nbk + t
   const int64_t bh = g / p.nbk, t = g % p.nbk;
-  const int j = threadIdx.x;
-  const uint8_t* row = p.k8 + g * kTileBytes + j * 128;
-  float kc[kD];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 31, h = lane >> 5;
+  const int key = 32 * w + col;
+  // B operand: channels 64h .. 64h + 63 of this lane's key, i.e. the logical
+  // 16-byte chunks 4h .. 4h + 3 of its row
+  const uint8_t* row = p.k8 + g * kTileBytes + key * 128;
+  float kb[64];
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    const uint4 u = *reinterpret_cast<const uint4*>(row + (((cc ^ swz(j)) & 7) << 4));
-    const int w[4] = {(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+  for (int c = 0; c < 4; ++c) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + ((((4 * h + c) ^ swz(key)) & 7) << 4));
+    const int wd[4] = {(int)u.x, (int)u.y, (int)u.z, (int)u.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (FP8) {
-        // E4M3 bytes -> values (exact in FP32)
-        kc[16 * cc + 4 * q + 0] = __builtin_amdgcn_cvt_f32_fp8(w[q], 0);
-        kc[16 * cc + 4 * q + 1] = __builtin_amdgcn_cvt_f32_fp8(w[q], 1);
-        kc[16 * cc + 4 * q + 2] = __builtin_amdgcn_cvt_f32_fp8(w[q], 2);
-        kc[16 * cc + 4 * q + 3] = __builtin_amdgcn_cvt_f32_fp8(w[q], 3);
+        kb[16 * c + 4 * q + 0] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 0);
+        kb[16 * c + 4 * q + 1] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 1);
+        kb[16 * c + 4 * q + 2] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 2);
+        kb[16 * c + 4 * q + 3] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 3);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kc[16 * cc + 4 * q + e] = (float)(int8_t)(w[q] >> (8 * e));
+        for (int e = 0; e < 4; ++e) kb[16 * c + 4 * q + e] = (float)(int8_t)(wd[q] >> (8 * e));
       }
     }
   }
   const float* qsr = p.q_scale + bh * p.nbq;
   const float* qm = p.q_mean + bh * p.nbq * kD;
-  float* out = p.ds + bh * p.nbq * (p.nbk * kBlk) + t * kBlk + j;
-  for (int64_t i0 = 0; i0 < p.nbq; i0 += kDsChunk) {
-    const int n = (int)(p.nbq - i0 < kDsChunk ? p.nbq - i0 : kDsChunk);
-    __syncthreads();
-    for (int x = j; x < n * kD; x += 128) sq[x / kD][x % kD] = qm[(i0 + x / kD) * kD + x % kD];
-    __syncthreads();
-    for (int i = 0; i < n; ++i) {
-      float acc = 0.0f;
+  float* out = p.ds + bh * p.nbq * (p.nbk * kBlk) + t * kBlk + key;
+  // A operand of a group of 32 Q blocks: this lane's block mean, divided by
+  // that block's u (one division per lane, then a multiply per mean)
+  auto load_a = [&](int64_t i0, float (&qa)[64]) __attribute__((always_inline)) {
+    const int64_t ia = i0 + col;
+    if (ia < p.nbq) {
+      const float4* src = reinterpret_cast<const float4*>(qm + ia * kD + 64 * h);
 #pragma unroll
-      for (int d = 0; d < kD; d += 4) {
-        const float4 m4 = *reinterpret_cast<const float4*>(&sq[i][d]);
-        acc = __builtin_fmaf(m4.x, kc[d], acc);
-        acc = __builtin_fmaf(m4.y, kc[d + 1], acc);
-        acc = __builtin_fmaf(m4.z, kc[d + 2], acc);
-        acc = __builtin_fmaf(m4.w, kc[d + 3], acc);
+      for (int c = 0; c < 16; ++c) {
+        const float4 m4 = src[c];
+        qa[4 * c] = m4.x; qa[4 * c + 1] = m4.y; qa[4 * c + 2] = m4.z; qa[4 * c + 3] = m4.w;
       }
-      const float u = qsr[i0 + i];
-      out[(i0 + i) * (p.nbk * kBlk)] = u > 0.0f ? __fdiv_rn(acc, u) : acc * 0x1p20f;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 64; ++c) qa[c] = 0.0f;
     }
+  };
+  auto scale_a = [&](int64_t i0, float (&qa)[64]) __attribute__((always_inline)) {
+    const int64_t ia = i0 + col;
+    const float u = ia < p.nbq ? qsr[ia] : 1.0f;
+    const float r = u > 0.0f ? __fdiv_rn(1.0f, u) : 0x1p20f;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) qa[c] *= r;
+  };
+  float qa[64], qn[64];
+  load_a(0, qa);
+  for (int64_t i0 = 0; i0 < p.nbq; i0 += 32) {
+    scale_a(i0, qa);
+    if (i0 + 32 < p.nbq) load_a(i0 + 32, qn);  // the next group's means, in flight during the MFMAs
+    f32x16 acc = {};
+#pragma unroll
+    for (int st = 0; st < 64; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[st], kb[st], acc, 0, 0, 0);
+    // accumulator row of register r: Q block i0 + 8(r / 4) + 4h + r % 4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (i < p.nbq) out[i * (p.nbk * kBlk)] = acc[r];
+    }
+#pragma unroll
+    for (int c = 0; c < 64; ++c) qa[c] = qn[c];
   }
 }
 
@@ -533,9 +562,9 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   DsP dp{a.packed + L.off_k8, q_scale, q_mean, reinterpret_cast<float*>(a.packed + L.off_ds),
          L.nbq, L.nbk, a.fp8qk ? 1 : 0};
   if (a.fp8qk)
-    hipLaunchKernelGGL(k_delta_s<true>, dim3((unsigned)(BH * L.nbk)), dim3(128), 0, stream, dp);
+    hipLaunchKernelGGL(k_delta_s<true>, dim3((unsigned)(BH * L.nbk)), dim3(256), 0, stream, dp);
   else
-    hipLaunchKernelGGL(k_delta_s<false>, dim3((unsigned)(BH * L.nbk)), dim3(128), 0, stream, dp);
+    hipLaunchKernelGGL(k_delta_s<false>, dim3((unsigned)(BH * L.nbk)), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
