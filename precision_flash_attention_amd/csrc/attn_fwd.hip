@@ -582,43 +582,66 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     accm += other_half_f(accm);
     shift = p.scale * (qscale * acc + accm);
   }
-  if (q < p.Nq) {
-    // (block-sparse: a row whose query block attends none of the listed
-    // tiles has l = 0, O = 0 and lse = -inf)
-    const float inv = SPARSE && lt == 0.0f ? 0.0f : 1.0f / lt;
-    if (p.splits == 1) {
-      uint16_t* orow = p.out + b * p.os0 + (int64_t)q * p.os1 + h * p.os2;
+  // (block-sparse: a row whose query block attends none of the listed
+  // tiles has l = 0, O = 0 and lse = -inf)
+  const float inv = SPARSE && lt == 0.0f ? 0.0f : 1.0f / lt;
+  if (p.splits == 1) {
+    // BF16 rows through 4 KiB of LDS per wave, 64 channels at a time: each
+    // lane holds 4-channel pieces of its row, so direct stores would write
+    // 8 bytes into each of 32 rows per instruction; staged, every global
+    // store writes whole 128-byte lines (8 lanes per row).  The area is the
+    // stage of the never-loaded tile nbk, whose last reader (tile nbk-3's
+    // PV) is two barriers back.  Chunks are XOR-swizzled by (row >> 1) & 7
+    // so the piece writes of 32 rows spread over the banks.  LDS operations
+    // of one wave run in order, so the second half's writes land after the
+    // first half's reads.
+    uint8_t* obuf = smem + (nbk % 3) * kStage + w * 4096;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int half = 0; half < 2; ++half) {
+      // (keeps the compiler from hoisting the second half's scale loads
+      // above the first half: fewer registers live at once)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int db2 = 0; db2 < 2; ++db2)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+          const int db = 2 * half + db2;
           const int d0 = 32 * db + 8 * a + 4 * hh;
           const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
           const float o0 = O[db][4 * a + 0] * sv.x * inv;
           const float o1 = O[db][4 * a + 1] * sv.y * inv;
           const float o2 = O[db][4 * a + 2] * sv.z * inv;
           const float o3 = O[db][4 * a + 3] * sv.w * inv;
-          *reinterpret_cast<uint2*>(orow + d0) =
+          const int c = 4 * db2 + a;
+          *reinterpret_cast<uint2*>(obuf + l32 * 128 + (((c ^ swz(l32)) & 7) << 4) + 8 * hh) =
               make_uint2(bf16_rne(o0) | (bf16_rne(o1) << 16), bf16_rne(o2) | (bf16_rne(o3) << 16));
         }
-      if (p.lse != nullptr && hh == 0) p.lse[bh * p.Nq + q] = lse + shift;
-    } else {
-      const int64_t row = ((int64_t)split * p.BH + bh) * p.Nq + q;
-      float* orow = p.opart + row * 128;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int d0 = 32 * db + 8 * a + 4 * hh;
-          const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
-          *reinterpret_cast<float4*>(orow + d0) =
-              make_float4(O[db][4 * a + 0] * sv.x * inv, O[db][4 * a + 1] * sv.y * inv,
-                          O[db][4 * a + 2] * sv.z * inv, O[db][4 * a + 3] * sv.w * inv);
-        }
-      if (hh == 0) p.lpart[row] = lse;
-      // the merge kernel adds the partials' lse to the shift left here
-      if (p.lse != nullptr && split == 0 && hh == 0) p.lse[bh * p.Nq + q] = shift;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const uint4 val = *reinterpret_cast<const uint4*>(obuf + r * 128 + (((c ^ swz(r)) & 7) << 4));
+        const int qr = q0 + r;
+        if (qr < p.Nq)
+          *reinterpret_cast<uint4*>(p.out + b * p.os0 + (int64_t)qr * p.os1 + h * p.os2 + 64 * half + 8 * c) = val;
+      }
     }
+    if (p.lse != nullptr && hh == 0 && q < p.Nq) p.lse[bh * p.Nq + q] = lse + shift;
+  } else if (q < p.Nq) {
+    const int64_t row = ((int64_t)split * p.BH + bh) * p.Nq + q;
+    float* orow = p.opart + row * 128;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * db + 8 * a + 4 * hh;
+        const float4 sv = *reinterpret_cast<const float4*>(vsc + d0);
+        *reinterpret_cast<float4*>(orow + d0) =
+            make_float4(O[db][4 * a + 0] * sv.x * inv, O[db][4 * a + 1] * sv.y * inv,
+                        O[db][4 * a + 2] * sv.z * inv, O[db][4 * a + 3] * sv.w * inv);
+      }
+    if (hh == 0) p.lpart[row] = lse;
+    // the merge kernel adds the partials' lse to the shift left here
+    if (p.lse != nullptr && split == 0 && hh == 0) p.lse[bh * p.Nq + q] = shift;
   }
 }
 
