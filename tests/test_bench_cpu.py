@@ -1,0 +1,60 @@
+"""Host logic of bench.py (CPU): algorithmic byte counts, the HBM traffic
+record and its digest gate, and the refusal of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+WAN = "wan-like video self-attention"
+
+
+def test_algorithmic_bytes_of_the_wan_workload():
+    B, H, N = 1, 40, 32760
+    nb = -(-N // 128)
+    # Q, K and V codes (1 byte each), the Q/K block scales and the V channel
+    # scales (4 bytes each), and the BF16 output
+    want = B * H * (3 * N * 128 + 4 * (2 * nb + 128) + 2 * N * 128)
+    assert bench.attn_algo_bytes(B, H, N, N) == want == 838758400
+    # BF16 Q, K, V read once; one code byte each written
+    assert bench.quant_unique_bytes(B, H, N, N) == 3 * B * H * N * 128 * 3 == 1509580800
+
+
+def _records():
+    with open(bench.TRAFFIC_RECORD) as fh:
+        return [json.loads(ln[len("traffic-record: "):]) for ln in fh if ln.startswith("traffic-record: ")]
+
+
+def test_traffic_record_is_reported_only_for_its_kernel():
+    recs = [r for r in _records() if r["workload"] == WAN]
+    assert {r["qk_format"] for r in recs} == {"int8", "fp8"}
+    digest = bench.attn_kernel_digest()
+    for r in recs:
+        got = bench.measured_traffic(WAN, r["qk_format"])
+        if r["kernel_digest"] != digest:
+            # counters of an older kernel are not reported
+            assert got is None
+            continue
+        # each counter scaled by what it read for a device copy of known size
+        want = (r["fetch_kib"] * r["copy_bytes"] / r["copy_fetch_kib"]
+                + r["write_kib"] * r["copy_bytes"] / r["copy_write_kib"])
+        assert got == int(round(want))
+        # at least the algorithmic bytes, the BF16 output written exactly once
+        assert got >= bench.attn_algo_bytes(1, 40, 32760, 32760)
+        assert abs(r["write_kib"] * 1024 - 2 * 32760 * 40 * 128) < 1024
+
+
+def test_traffic_is_null_for_other_kernels_and_workloads(monkeypatch):
+    assert bench.measured_traffic("text cross-attention", "int8") is None
+    monkeypatch.setattr(bench, "attn_kernel_digest", lambda: "0" * 16)
+    assert bench.measured_traffic(WAN, "int8") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
