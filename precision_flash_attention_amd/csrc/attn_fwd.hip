@@ -491,7 +491,15 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     asm volatile("" ::"v"(l_run));
   };
 
-  auto barrier = [] { __builtin_amdgcn_s_barrier(); };
+  // The barrier builtin does not order memory for the compiler: the empty
+  // asm with a memory clobber on each side keeps every LDS access (the
+  // tile reads, the epilogue's staging) on its side of the barrier.  It
+  // adds no instruction and no wait.
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
 #pragma unroll
