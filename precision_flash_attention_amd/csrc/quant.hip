@@ -35,6 +35,7 @@ namespace sattn {
 namespace {
 
 constexpr float kFltMin = 1.17549435e-38f;  // 2^-126
+constexpr int64_t kStatsBlkBelow = 2 * 256 * 16;  // (b, block, head) triples: 2 k_stats workgroups per CU
 
 __device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -115,6 +116,76 @@ __global__ __launch_bounds__(256) void k_stats(StatsP p) {
   ko[1] = make_float4(s[4], s[5], s[6], s[7]);
   vo[0] = make_float4(m[0], m[1], m[2], m[3]);
   vo[1] = make_float4(m[4], m[5], m[6], m[7]);
+}
+
+// The same partials for short key sequences, where k_stats has a few
+// workgroups whose threads each wait on 16 dependent rounds of loads.  One
+// workgroup per (b, key block, head): every thread loads its 8 rows of K and
+// V at once (16 bytes of one row per thread, 16 threads per row), the V
+// maxima are reduced through LDS, and K is staged in LDS so that 16 threads
+// can then add its rows in token order, the order k_stats uses.
+__global__ __launch_bounds__(256) void k_stats_blk(StatsP p) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kBlk * kD];  // the K block, 32 KiB
+  __shared__ float vred[16][kD];                                  // V maxima per row group
+  const int64_t wg = blockIdx.x;  // (b, t, h), h fastest
+  const int64_t h = wg % p.H;
+  const int64_t t = (wg / p.H) % p.nbk;
+  const int64_t b = wg / p.H / p.nbk;
+  const int tid = threadIdx.x;
+  const int g = tid & 15, rg = tid >> 4;  // channels 8g..8g+7 of rows rg + 16 i
+  const int64_t n0 = t * kBlk;
+  const int nv = (int)(p.Nkv - n0 < kBlk ? p.Nkv - n0 : kBlk);  // valid rows of the block
+  const uint16_t* kp = p.k + b * p.ks0 + h * p.ks2 + 8 * g;
+  const uint16_t* vp = p.v + b * p.vs0 + h * p.vs2 + 8 * g;
+  uint4 kk[8], vv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = rg + 16 * i;
+    kk[i] = vv[i] = make_uint4(0, 0, 0, 0);
+    if (row < nv) {
+      kk[i] = *reinterpret_cast<const uint4*>(kp + (n0 + row) * p.ks1);
+      vv[i] = *reinterpret_cast<const uint4*>(vp + (n0 + row) * p.vs1);
+    }
+  }
+  float m[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) m[c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = rg + 16 * i;
+    if (row < nv) {
+      float vf[8];
+      unpack8(vv[i], vf);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], fabsf(vf[c]));
+      *reinterpret_cast<uint4*>(kt + row * kD + 8 * g) = kk[i];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) vred[rg][8 * g + c] = m[c];
+  __syncthreads();
+  const int64_t o = ((b * p.H + h) * p.nbk + t) * kD;
+  if (tid < 16) {
+    float s[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] = 0.0f;
+#pragma unroll 8
+    for (int n = 0; n < nv; ++n) {
+      float kf[8];
+      unpack8(*reinterpret_cast<const uint4*>(kt + n * kD + 8 * tid), kf);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[c] = s[c] + kf[c];
+    }
+    float4* ko = reinterpret_cast<float4*>(p.kpart + o + 8 * tid);
+    ko[0] = make_float4(s[0], s[1], s[2], s[3]);
+    ko[1] = make_float4(s[4], s[5], s[6], s[7]);
+  } else if (tid < 16 + kD) {
+    const int c = tid - 16;
+    float mm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mm = fmaxf(mm, vred[r][c]);
+    p.vpart[o + c] = mm;
+  }
 }
 
 // Q smoothing: per (b, Q block t, head, 8-channel group) the FP32 sum of the
@@ -532,8 +603,15 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
 
   StatsP sp{a.k, a.v, a.k_str[0], a.k_str[1], a.k_str[2], a.v_str[0], a.v_str[1], a.v_str[2],
             L.B, L.H, L.Nkv, L.nbk, kpart, vpart};
-  const int64_t sthreads = L.B * L.nbk * L.H * 16;
-  hipLaunchKernelGGL(k_stats, dim3((unsigned)((sthreads + 255) / 256)), dim3(256), 0, stream, sp);
+  // k_stats runs one thread per (b, block, head, 8 channels); below two of
+  // its workgroups per CU the per-block kernel is faster (same values)
+  const int64_t sblocks = L.B * L.nbk * L.H;
+  if (sblocks < kStatsBlkBelow) {
+    hipLaunchKernelGGL(k_stats_blk, dim3((unsigned)sblocks), dim3(256), 0, stream, sp);
+  } else {
+    const int64_t sthreads = sblocks * 16;
+    hipLaunchKernelGGL(k_stats, dim3((unsigned)((sthreads + 255) / 256)), dim3(256), 0, stream, sp);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   float* q_mean = L.qsmooth ? reinterpret_cast<float*>(a.packed + L.off_qm) : nullptr;
