@@ -58,26 +58,27 @@ def _check_max_err(o_gpu_bits, o_ref_bits, v_bits, what):
     assert err <= MAX_ERR and c >= MIN_COS, (what, err, c)
 
 
-def test_longest_key_sequence(device):
-    log(f"max sizes: Nkv = 2^24 (K = 0, V = one 128-token block x {REPS}), Nq = 128")
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_longest_key_sequence(device, fmt):
+    log(f"max sizes ({fmt} Q/K): Nkv = 2^24 (K = 0, V = one 128-token block x {REPS}), Nq = 128")
     q, vb = _period_inputs(seed=31)
     v = np.ascontiguousarray(vb[:, :PERIOD])
     k0 = np.zeros_like(v)
     # one period, GPU and oracle
-    small = sattn.quantize_qkv(to_dev(q), to_dev(k0), to_dev(v))
-    want = oracle.quantize(q, k0, v)
+    small = sattn.quantize_qkv(to_dev(q), to_dev(k0), to_dev(v), qk_format=fmt)
+    want = oracle.quantize(q, k0, v, qk_format=fmt)
     got_small = _unpack_codes(small)
     assert_codes_equal(got_small, want)
     o_ref, lse_ref = oracle.attention(want, SCALE, return_lse=True)
     # full length
     kd = torch.zeros((1, NMAX, 1, 128), dtype=torch.bfloat16, device=device)
     vd = _tiled(v)
-    big = sattn.quantize_qkv(to_dev(q), kd, vd)
+    big = sattn.quantize_qkv(to_dev(q), kd, vd, qk_format=fmt)
     torch.cuda.synchronize()
     del kd, vd
     log("  quantized; unpacking")
     got = _unpack_codes(big)
-    assert np.array_equal(got["q8"], got_small["q8"])
+    assert np.array_equal(got["q8"].view(np.uint8), got_small["q8"].view(np.uint8))
     assert np.array_equal(got["q_scale"].view(np.uint32), got_small["q_scale"].view(np.uint32))
     assert not got["k8"].any() and not got["k_scale"].any() and not got["k_mean"].any()
     assert np.array_equal(got["v_scale"].view(np.uint32), want["v_scale"].view(np.uint32))
@@ -96,23 +97,24 @@ def test_longest_key_sequence(device):
         assert d <= 2e-5, d
 
 
-def test_longest_query_sequence(device):
-    log(f"max sizes: Nq = 2^24 (Q = one 128-token block x {REPS}), Nkv = 256 (K = 0)")
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_longest_query_sequence(device, fmt):
+    log(f"max sizes ({fmt} Q/K): Nq = 2^24 (Q = one 128-token block x {REPS}), Nkv = 256 (K = 0)")
     q, v = _period_inputs(seed=32)
     k0 = np.zeros_like(v)
-    small = sattn.quantize_qkv(to_dev(q), to_dev(k0), to_dev(v))
-    want = oracle.quantize(q, k0, v)
+    small = sattn.quantize_qkv(to_dev(q), to_dev(k0), to_dev(v), qk_format=fmt)
+    want = oracle.quantize(q, k0, v, qk_format=fmt)
     got_small = _unpack_codes(small)
     assert_codes_equal(got_small, want)
     o_ref = oracle.attention(want, SCALE)                    # [1, 128, 1, 128] BF16 bits
     qd = _tiled(q)
-    big = sattn.quantize_qkv(qd, to_dev(k0), to_dev(v))
+    big = sattn.quantize_qkv(qd, to_dev(k0), to_dev(v), qk_format=fmt)
     torch.cuda.synchronize()
     del qd
     log("  quantized; unpacking")
     got = _unpack_codes(big)
-    q8 = got["q8"].reshape(REPS, PERIOD, 128)
-    bad = np.flatnonzero((q8 != want["q8"].reshape(1, PERIOD, 128)).any(axis=(1, 2)))
+    q8 = got["q8"].view(np.uint8).reshape(REPS, PERIOD, 128)
+    bad = np.flatnonzero((q8 != want["q8"].view(np.uint8).reshape(1, PERIOD, 128)).any(axis=(1, 2)))
     assert bad.size == 0, f"Q codes of {bad.size} periods differ, first {bad[:5].tolist()}"
     qs = got["q_scale"].reshape(-1).view(np.uint32)
     assert np.all(qs == want["q_scale"].reshape(-1).view(np.uint32)[0])
