@@ -17,7 +17,10 @@ Printed: one JSON line.  value = 4*B*H*Nq*Nkv*D / (time of one step), in
 TFLOP/s; attention-only and quantize-only figures, the roofline of the
 attention kernel (its average duration from HIP events recorded on the
 stream it runs on) and the CPU oracle's rate on a bounded sample are
-reported beside it.
+reported beside it.  gpu_clock holds the shader clock and board power
+sampled from sysfs during the timed steps (null where the host does not
+expose them for exactly one GPU), and attention_only.frac_of_peak_at_sclk
+the attention rate against the peak scaled to that clock.
 """
 import argparse
 import hashlib
@@ -25,6 +28,7 @@ import json
 import math
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +88,65 @@ def measured_traffic(workload, qk_format):
     return int(round(fetch + write))
 
 
+PEAK_SCLK_MHZ = 2400.0    # the clock the 5.0 PFLOP/s peak is quoted at
+
+
+def sclk_from_dpm(text):
+    """Current shader clock in MHz from the text of a pp_dpm_sclk file: the
+    level marked with '*'; None if no line is marked."""
+    for ln in text.splitlines():
+        if ln.rstrip().endswith("*"):
+            num = "".join(ch for ch in ln.split(":", 1)[-1] if ch.isdigit() or ch == ".")
+            return float(num) if num else None
+    return None
+
+
+def gpu_sysfs_dir():
+    """The DRM device directory of the GPU when exactly one GPU on the host
+    exposes its shader clock (pp_dpm_sclk); otherwise None (which card is
+    cuda:0 is then not known)."""
+    import glob
+    cands = [d for d in sorted(glob.glob("/sys/class/drm/card*/device"))
+             if os.path.exists(os.path.join(d, "pp_dpm_sclk"))]
+    return cands[0] if len(cands) == 1 else None
+
+
+class ClockSampler(threading.Thread):
+    """Samples the shader clock and the board power from sysfs every
+    `period` seconds while the timed steps run."""
+
+    def __init__(self, sysdir, period=0.02):
+        super().__init__(daemon=True)
+        self.sysdir, self.period = sysdir, period
+        self.sclk, self.power = [], []
+        self.stop = threading.Event()
+        import glob
+        pw = glob.glob(os.path.join(sysdir, "hwmon", "hwmon*", "power1_input"))
+        self.power_file = pw[0] if len(pw) == 1 else None
+
+    def run(self):
+        while not self.stop.is_set():
+            try:
+                with open(os.path.join(self.sysdir, "pp_dpm_sclk")) as fh:
+                    mhz = sclk_from_dpm(fh.read())
+                if mhz is not None:
+                    self.sclk.append(mhz)
+                if self.power_file is not None:
+                    with open(self.power_file) as fh:
+                        self.power.append(int(fh.read().strip()) / 1e6)   # microwatts -> W
+            except (OSError, ValueError):
+                pass
+            self.stop.wait(self.period)
+
+    def summary(self):
+        if not self.sclk:
+            return None
+        med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+        return {"sclk_mhz_median": med(self.sclk), "sclk_mhz_min": min(self.sclk),
+                "sclk_mhz_max": max(self.sclk), "power_w_median": med(self.power) if self.power else None,
+                "samples": len(self.sclk), "source": "sysfs pp_dpm_sclk, hwmon power1_input"}
+
+
 def copy_calibration(torch, dev):
     """Plain device-to-device copies of a known size, for scaling the HBM
     byte counters (FETCH_SIZE / WRITE_SIZE) of the other kernels."""
@@ -135,6 +198,8 @@ def main():
     ap.add_argument("--lse", action="store_true", help="also write the per-row LSE")
     ap.add_argument("--q-smooth", action="store_true",
                     help="Q smoothing per 128-token block with the Delta-S correction")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the shader clock and board power during the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -188,6 +253,10 @@ def main():
     torch.cuda.synchronize()
 
     events = []
+    sysdir = None if args.no_clock else gpu_sysfs_dir()
+    sampler = ClockSampler(sysdir) if sysdir is not None else None
+    if sampler is not None:
+        sampler.start()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -197,6 +266,11 @@ def main():
         events.append(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = None
+    if sampler is not None:
+        sampler.stop.set()
+        sampler.join()
+        clock = sampler.summary()
     ms_step = wall * 1e3 / args.steps
     t_quant = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     t_attn = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
@@ -206,6 +280,10 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tf = flops / (t_attn * 1e-3) / 1e12
     qbytes = quant_unique_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv)
+    # the same rate against the peak scaled to the clock the GPU ran at
+    frac_at_sclk = None
+    if clock is not None:
+        frac_at_sclk = round(attn_tf / (PEAK_TFLOPS * clock["sclk_mhz_median"] / PEAK_SCLK_MHZ), 4)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -226,10 +304,12 @@ def main():
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "attended_fraction": round(flops / (4 * cfg.B * cfg.H * cfg.Nq * cfg.Nkv * 128), 4),
         "attention_only": {"ms": round(t_attn, 4), "ms_min": round(t_attn_min, 4),
-                           "tflops": round(attn_tf, 2), "frac_of_peak": round(attn_tf / PEAK_TFLOPS, 4)},
+                           "tflops": round(attn_tf, 2), "frac_of_peak": round(attn_tf / PEAK_TFLOPS, 4),
+                           "frac_of_peak_at_sclk": frac_at_sclk},
         "quantize": {"ms": round(t_quant, 4), "unique_bytes": qbytes,
                      "gbs": round(qbytes / (t_quant * 1e-3) / 1e9, 1),
                      "frac_of_hbm_peak": round(qbytes / (t_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "gpu_clock": clock,
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(attn_tf, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(cfg.name, args.qk_format),

@@ -58,3 +58,11 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_shader_clock_parser():
+    # the current clock between levels ("S:" line) and on a level
+    assert bench.sclk_from_dpm("S: 120Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == 120.0
+    assert bench.sclk_from_dpm("0: 500Mhz\n1: 2400Mhz *\n") == 2400.0
+    assert bench.sclk_from_dpm("0: 500Mhz\n1: 2400Mhz\n") is None
+    assert bench.sclk_from_dpm("") is None
