@@ -275,6 +275,7 @@ def main():
     t_quant = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     t_attn = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     t_attn_min = min(e[1].elapsed_time(e[2]) for e in events)
+    t_attn_med = sorted(e[1].elapsed_time(e[2]) for e in events)[len(events) // 2]
 
     flops = cfg.flops
     value = flops / (ms_step * 1e-3) / 1e12
@@ -303,7 +304,7 @@ def main():
                                                        "sattn_fwd" if cfg.Nq == cfg.Nkv else "sattn_fwd_cross")),
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "attended_fraction": round(flops / (4 * cfg.B * cfg.H * cfg.Nq * cfg.Nkv * 128), 4),
-        "attention_only": {"ms": round(t_attn, 4), "ms_min": round(t_attn_min, 4),
+        "attention_only": {"ms": round(t_attn, 4), "ms_median": round(t_attn_med, 4), "ms_min": round(t_attn_min, 4),
                            "tflops": round(attn_tf, 2), "frac_of_peak": round(attn_tf / PEAK_TFLOPS, 4),
                            "frac_of_peak_at_sclk": frac_at_sclk},
         "quantize": {"ms": round(t_quant, 4), "unique_bytes": qbytes,
