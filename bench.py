@@ -18,9 +18,10 @@ TFLOP/s; attention-only and quantize-only figures, the roofline of the
 attention kernel (its average duration from HIP events recorded on the
 stream it runs on) and the CPU oracle's rate on a bounded sample are
 reported beside it.  gpu_clock holds the shader clock and board power
-sampled from sysfs during the timed steps (null where the host does not
-expose them for exactly one GPU), and attention_only.frac_of_peak_at_sclk
-the attention rate against the peak scaled to that clock.
+sampled from sysfs every 20 ms during the timed steps (null where the host
+does not expose them for exactly one GPU, or where the steps take under
+five sampling periods), and attention_only.frac_of_peak_at_sclk the
+attention rate against the peak scaled to that clock.
 """
 import argparse
 import hashlib
@@ -115,6 +116,8 @@ class ClockSampler(threading.Thread):
     """Samples the shader clock and the board power from sysfs every
     `period` seconds while the timed steps run."""
 
+    MIN_SAMPLES = 5
+
     def __init__(self, sysdir, period=0.02):
         super().__init__(daemon=True)
         self.sysdir, self.period = sysdir, period
@@ -139,7 +142,9 @@ class ClockSampler(threading.Thread):
             self.stop.wait(self.period)
 
     def summary(self):
-        if not self.sclk:
+        # a step sequence shorter than a few sampling periods is seen only
+        # while the clock ramps up: no figure then
+        if len(self.sclk) < self.MIN_SAMPLES:
             return None
         med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
         return {"sclk_mhz_median": med(self.sclk), "sclk_mhz_min": min(self.sclk),

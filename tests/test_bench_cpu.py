@@ -66,3 +66,13 @@ def test_shader_clock_parser():
     assert bench.sclk_from_dpm("0: 500Mhz\n1: 2400Mhz *\n") == 2400.0
     assert bench.sclk_from_dpm("0: 500Mhz\n1: 2400Mhz\n") is None
     assert bench.sclk_from_dpm("") is None
+
+
+def test_clock_summary_needs_several_samples(tmp_path):
+    s = bench.ClockSampler(str(tmp_path))
+    s.sclk = [783.0]
+    assert s.summary() is None
+    s.sclk = [1700.0, 1800.0, 1750.0, 1900.0, 1200.0]
+    s.power = [1000.0] * 5
+    got = s.summary()
+    assert got["sclk_mhz_median"] == 1750.0 and got["sclk_mhz_min"] == 1200.0 and got["samples"] == 5
