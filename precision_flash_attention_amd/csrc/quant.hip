@@ -122,8 +122,9 @@ __global__ __launch_bounds__(256) void k_stats(StatsP p) {
 // workgroups whose threads each wait on 16 dependent rounds of loads.  One
 // workgroup per (b, key block, head): every thread loads its 8 rows of K and
 // V at once (16 bytes of one row per thread, 16 threads per row), the V
-// maxima are reduced through LDS, and K is staged in LDS so that 16 threads
-// can then add its rows in token order, the order k_stats uses.
+// maxima are reduced through LDS, and K is staged in LDS so that 128 threads,
+// one per channel, can then add its rows in token order, the order k_stats
+// uses.
 __global__ __launch_bounds__(256) void k_stats_blk(StatsP p) {
   __shared__ __attribute__((aligned(16))) uint16_t kt[kBlk * kD];  // the K block, 32 KiB
   __shared__ float vred[16][kD];                                  // V maxima per row group
@@ -165,22 +166,14 @@ __global__ __launch_bounds__(256) void k_stats_blk(StatsP p) {
   for (int c = 0; c < 8; ++c) vred[rg][8 * g + c] = m[c];
   __syncthreads();
   const int64_t o = ((b * p.H + h) * p.nbk + t) * kD;
-  if (tid < 16) {
-    float s[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) s[c] = 0.0f;
-#pragma unroll 8
-    for (int n = 0; n < nv; ++n) {
-      float kf[8];
-      unpack8(*reinterpret_cast<const uint4*>(kt + n * kD + 8 * tid), kf);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s[c] = s[c] + kf[c];
-    }
-    float4* ko = reinterpret_cast<float4*>(p.kpart + o + 8 * tid);
-    ko[0] = make_float4(s[0], s[1], s[2], s[3]);
-    ko[1] = make_float4(s[4], s[5], s[6], s[7]);
-  } else if (tid < 16 + kD) {
-    const int c = tid - 16;
+  if (tid < kD) {
+    // one channel per thread, its rows in token order
+    float s = 0.0f;
+#pragma unroll 16
+    for (int n = 0; n < nv; ++n) s = s + __uint_as_float((uint32_t)kt[n * kD + tid] << 16);
+    p.kpart[o + tid] = s;
+  } else {
+    const int c = tid - kD;
     float mm = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mm = fmaxf(mm, vred[r][c]);
