@@ -389,7 +389,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   };
 
   // ---- V(t): online softmax of S -> P, conditional rescale of O
-  auto vblock = [&]() __attribute__((always_inline)) {
+  // first: the sweep's first tile (m = -inf, O = 0 and l = 0 before it), where
+  // the rescale would multiply zeros by exp2(-inf); the block-sparse instance
+  // keeps it, since its first attended tile depends on the table
+  auto vblock = [&](bool first) __attribute__((always_inline)) {
     if constexpr (SPARSE) {
       pv_skip = masked_cur;
       if (masked_cur) return;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       mt = (__int_as_float(mx) - kMagicF) * c;
     }
     const float mnew = fmaxf(m_run, mt);
-    if (__any(mnew > m_run)) {
+    if (!(first && !SPARSE) && __any(mnew > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
       l_run *= alpha;
 #pragma unroll
@@ -522,7 +525,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   auto step = [&](int t, bool do_pv, int kst) __attribute__((always_inline)) {
     mblock(t, do_pv, true, kst, 128, SPARSE && !group_attends(t));
     barrier();
-    vblock();
+    vblock(!do_pv);
     if (isA) wait_loads();
     barrier();
   };
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   for (; t < last; ++t) step(t, true, t % 3);
   mblock(last, last > 0, true, last % 3, rem, SPARSE && !group_attends(last));
   barrier();
-  vblock();
+  vblock(last == 0);
   if (isA) wait_loads();
   barrier();
   mblock(nbk, true, false, nbk % 3, 128, false);
