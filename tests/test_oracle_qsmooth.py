@@ -72,6 +72,37 @@ def test_means_are_the_block_means():
     assert np.all(resid <= 127 * qs * (1 + 1e-6))
 
 
+def test_q_mean_sums_in_token_order():
+    # integer-valued BF16 inputs whose FP32 sum depends on the order: channel
+    # 0 of block 0 holds 2^24, then 126 ones, then -2^24.  In token order
+    # every 2^24 + 1 rounds back to 2^24 (ties to even), so the sum is
+    # exactly 0; reversed, -2^24 + 1 + ... is exact and gives 126; a pairwise
+    # tree gives (2^24 + 1) -> 2^24, 2 * 62 pairs of ones, and 1 - 2^24 at the
+    # end, which is neither.  Channel 1 holds the same values in the reverse
+    # token order (sum 126).  Channel 2 repeats (2^24, 1, -2^24, 1): in token
+    # order the running sum is back at 1 after every four tokens (2^24 + 1
+    # and 1 + 2^24 both round to 2^24), so the sum is 1; a pairwise tree
+    # gives 32 (each group of four sums to 2^24 - 16777215 = 1) and the
+    # reverse order 64.
+    n = 128
+    ch0 = np.array([2.0 ** 24] + [1.0] * 126 + [-(2.0 ** 24)])
+    ch2 = np.array([2.0 ** 24 if i % 4 == 0 else -(2.0 ** 24) if i % 4 == 2 else 1.0 for i in range(n)])
+    qf = np.zeros((1, n, 1, D))
+    qf[0, :, 0, 0] = ch0
+    qf[0, :, 0, 1] = ch0[::-1]
+    qf[0, :, 0, 2] = ch2
+    q = bf16_of(qf)
+    assert np.array_equal(f64(q)[0, :, 0, :3], qf[0, :, 0, :3])          # exact in BF16
+    _, k, v = testkit.make_inputs(testkit.CONFIGS[1], seed=5, H=1, Nq=n, Nkv=n)
+    c = oracle.quantize(q, k, v, q_smooth=True)
+    m = c["q_mean"][0, 0, 0].astype(np.float64)
+    # token order, by hand: 0 / 128, 126 / 128 and 1 / 128
+    assert m[0] == 0.0
+    assert m[1] == 126.0 / 128.0
+    assert m[2] == 1.0 / 128.0
+    assert np.all(m[3:] == 0.0)
+
+
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])
 def test_block_shift_of_q_changes_only_delta_s(fmt):
     # adding a per-block vector c_b to every query of block b (1/8 grid, exact
