@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "layout.h"
 
@@ -406,7 +408,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     if constexpr (QSMOOTH) {
       // add Delta-S (in the units of S: the table holds (qmean . kcode) / qs)
       // of this group's query block to every score, written back over S,
-      // then the row maximum on floats; masked keys stay -inf
+      // then the row maximum on floats; masked keys stay -inf.  For INT8 the
+      // accumulator's bias is taken off first (exact: both are integers
+      // below 2^24), so the sum is rounded at the score's own magnitude.
       const float* dsl = reinterpret_cast<const float*>(smem + dstage_cur * kStage + 2 * kTileBytes) +
                          (isA ? 0 : 128) + 4 * hh;
       float mx = -__builtin_inff();
@@ -419,13 +423,14 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
           for (int b2 = 0; b2 < 4; ++b2) {
             const int r = 4 * a + b2;
-            const float tt = __int_as_float(S[kb][r]) + dv[b2];
+            const float sv = FP8QK ? __int_as_float(S[kb][r]) : __int_as_float(S[kb][r]) - kMagicF;
+            const float tt = sv + dv[b2];
             S[kb][r] = __float_as_int(tt);
             mx = fmaxf(mx, tt);
           }
         }
       mx = fmaxf(mx, other_half_f(mx));
-      mt = FP8QK ? mx * c : (mx - kMagicF) * c;
+      mt = mx * c;
     } else if constexpr (FP8QK) {
       // FP32 scores (unscaled); masked keys are -inf
       float mx = -__builtin_inff();
@@ -454,14 +459,14 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
     m_run = mnew;
-    // exponent argument fma(S_f, c, nb) = (score - m) log2 e + log2 448; for
-    // INT8 codes the float view of S carries the bias 1.5 * 2^23, folded into
-    // nb.  Rounding that nb to FP32 moves the tile's reference point by up to
-    // 0.75 c; the block-sparse instance, whose rows may see few tiles, instead
-    // subtracts the bias from each score (exact) at one more VALU operation
-    // per score.
-    constexpr bool kFoldBias = !FP8QK && !SPARSE;
-    float nb = kFoldBias ? __builtin_fmaf(-kMagicF, c, kLog2_448 - mnew) : kLog2_448 - mnew;
+    // exponent argument fma(s, c, nb) = (score - m) log2 e + log2 448 with
+    // nb = log2 448 - m, rounded once.  For INT8 codes the float view of S
+    // carries the bias 1.5 * 2^23; it is subtracted from each score (exact)
+    // rather than folded into nb, because nb - 1.5 * 2^23 c would be rounded
+    // at the magnitude of 1.5 * 2^23 c: a per-tile shift of the reference
+    // point that moves P's E4M3 rounding and reweights a row's tiles, by
+    // more than the accuracy bar at sharp softmax scales.
+    const float nb = kLog2_448 - mnew;
     float ls[4];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float sf = __int_as_float(S[kb][r0 + i]);
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(FP8QK || kFoldBias ? sf : sf - kMagicF, c, nb));
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(FP8QK || QSMOOTH ? sf : sf - kMagicF, c, nb));
           // the first term starts the sum (p >= 0, so 0 + p == p)
           ls[i] = (g == 0 && j == 0) ? pv[i] : ls[i] + pv[i];
         }
@@ -738,18 +743,19 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
   constexpr int BM = 256;
   constexpr int kLds = 3 * (kStageBytes + (QSMOOTH ? 1024 : 0));
-  // Raising the dynamic LDS limit is per function and device, once each
-  // (a repeated call from a racing thread is harmless).
+  // Raising the dynamic LDS limit is per function and device, once each.
+  // The flags are atomics: threads that race here may both set the
+  // attribute (the same value, harmless), with no unsynchronised access.
   constexpr int kMaxDev = 64;
-  static bool attr_set[kMaxDev] = {};
+  static std::atomic<bool> attr_set[kMaxDev];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDev || !attr_set[dev]) {
+  if (dev < 0 || dev >= kMaxDev || !attr_set[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_pp_kernel<FP8QK, SPARSE, QSMOOTH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDev) attr_set[dev] = true;
+    if (dev >= 0 && dev < kMaxDev) attr_set[dev].store(true, std::memory_order_release);
   }
   AttnP p;
   p.q8 = a.packed + L.off_q8;

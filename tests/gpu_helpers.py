@@ -77,3 +77,149 @@ def sample_rows(B: int, H: int, Nq: int, per_head: int, seed: int) -> np.ndarray
             idx.update({0, Nq - 1, max(0, Nq - 129), (Nq // 128) * 128 if (Nq // 128) * 128 < Nq else 0})
             rows.extend((b, h, i) for i in sorted(idx))
     return np.array(rows, dtype=np.int64)
+
+
+def sample_rows_strided(B: int, H: int, Nq: int, stride: int, seed: int) -> np.ndarray:
+    """One row in every `stride` consecutive query rows of every (b, h), at a
+    seeded offset inside the group, plus each head's first and last row and
+    the rows around its last full 128-row block.  With stride 32 every wave's
+    32 queries are represented (and so every workgroup, query tile and
+    position of the workgroup-to-XCD mapping)."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, Nq, stride)
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            off = rng.integers(0, stride, size=starts.size)
+            idx = np.minimum(starts + off, Nq - 1)
+            extra = [0, Nq - 1, max(0, Nq - 129)]
+            if (Nq // 128) * 128 < Nq:
+                extra.append((Nq // 128) * 128)
+            idx = np.unique(np.concatenate([idx, np.array(extra, dtype=np.int64)]))
+            rows.append(np.stack([np.full(idx.size, b), np.full(idx.size, h), idx], axis=1))
+    return np.concatenate(rows).astype(np.int64)
+
+
+# rows per sample group at full size: every wave of the Wan-like and
+# cross-attention workloads, every other wave of the long-sequence one
+# (whose rows cost twice as much in the oracle)
+FULL_SIZE_STRIDE = {3: 32, 4: 32, 5: 64}
+
+
+# FP8 Q/K format: v_mfma_scale_f32_32x32x64_f8f6f4 does not return the
+# correctly rounded sum of its products (the INT8 instruction is exact).
+# Its error is bounded here by FP8_DOT_REL times the sum of the products'
+# magnitudes; a score error of at most delta_i (natural-log units) on row i
+# moves that row's output by at most 2 delta_i max|V| to first order.
+FP8_DOT_REL = 2.0 ** -11
+
+
+def fp8_score_error(codes, scale, rows=None) -> np.ndarray:
+    """delta per query row: FP8_DOT_REL * max_j sum_d |q_id k_jd| qs_i ks_j
+    * softmax_scale, from the oracle's codes.  [B, H, Nq], or [n] for
+    rows[:, (b, h, i)]."""
+    B, H, Nq, _ = codes["q8"].shape
+    Nkv = codes["k8"].shape[2]
+    dec = lambda c: np.abs(oracle.e4m3_decode(c.view(np.uint8)))  # noqa: E731
+    out = np.zeros((B, H, Nq)) if rows is None else np.zeros(len(rows))
+    for b in range(B):
+        for h in range(H):
+            if rows is None:
+                qi = np.arange(Nq)
+                sel = None
+            else:
+                sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
+                if sel.size == 0:
+                    continue
+                qi = rows[sel, 2]
+            qa = dec(codes["q8"][b, h, qi]) * codes["q_scale"][b, h][qi // 128].astype(np.float64)[:, None]
+            ka = dec(codes["k8"][b, h]) * codes["k_scale"][b, h][np.arange(Nkv) // 128].astype(np.float64)[:, None]
+            worst = np.zeros(len(qi))
+            for j0 in range(0, Nkv, 8192):
+                worst = np.maximum(worst, (qa @ np.ascontiguousarray(ka[j0:j0 + 8192].T)).max(axis=1))
+            d = FP8_DOT_REL * worst * scale
+            if sel is None:
+                out[b, h] = d
+            else:
+                out[sel] = d
+    return out
+
+
+def out_bar(codes, scale, rows=None):
+    """Per-row bar on max_d |O_gpu - O_oracle| / max|V|: 2e-2, plus 2 delta_i
+    in the FP8 Q/K format.  [B, H, Nq], or [n] for rows."""
+    if codes.get("qk_format", "int8") != "fp8":
+        B, H, Nq, _ = codes["q8"].shape
+        return np.full((B, H, Nq) if rows is None else (len(rows),), MAX_ERR)
+    return MAX_ERR + 2.0 * fp8_score_error(codes, scale, rows)
+
+
+def row_errors(o_gpu_bits: np.ndarray, o_orc_bits: np.ndarray, max_abs_v: float) -> np.ndarray:
+    """max_d |O_gpu - O_oracle| / max|V| per row: [B, H, Nq] from BSHD
+    outputs, or [n] from [n, 128] rows."""
+    a = testkit.bf16_to_f32(o_gpu_bits).astype(np.float64)
+    b = testkit.bf16_to_f32(o_orc_bits).astype(np.float64)
+    e = np.abs(a - b).max(axis=-1) / max_abs_v
+    return np.transpose(e, (0, 2, 1)) if e.ndim == 3 else e
+
+
+def check_rows(o_gpu_bits, o_orc_bits, v_bits, bar_rows, what, min_cos=MIN_COS):
+    """Every row within its bar and the global cosine >= min_cos; returns
+    (worst error / bar, max error, cosine)."""
+    mv = float(np.abs(testkit.bf16_to_f32(v_bits)).max())
+    e = row_errors(o_gpu_bits, o_orc_bits, mv)
+    _, c = parity(o_gpu_bits, o_orc_bits, mv)
+    ratio = float(np.max(e / bar_rows)) if e.size else 0.0
+    log(f"  {what}: max err / max|V| = {float(e.max()):.3e}, worst err / bar = {ratio:.3f} "
+        f"(bar {float(np.min(bar_rows)):.2e}..{float(np.max(bar_rows)):.2e}), cos = {c:.7f}")
+    assert ratio <= 1.0 and c >= min_cos, (ratio, c)
+    return ratio, float(e.max()), c
+
+
+def lse_bar(codes, scale, rows=None) -> np.ndarray:
+    """Per-row bar on |lse_gpu - lse_oracle| (natural log), derived from the
+    kernel's FP32 steps (u = 2^-24):
+      - the dequantisation constant c = fl(fl(qs ks) fl(scale log2 e)) and
+        the row maximum m = fl(acc c) carry <= 5u relative error, and with
+        Q smoothing the FP32 sums acc + Delta-S and the Delta-S products
+        <= 129u: 2^-17 * smag, smag = max_j sum_d q~_id |k~_jd| * scale;
+      - the K-mean shift, a 64-term FMA chain per lane plus one add:
+        2^-17 * sum_d q~_id |kmean_d| * scale;
+      - the FP32 row sum of at most Nkv positive terms, rescaled at most
+        once per key tile by an exp2 within 2u: (Nkv + 2 nbk) u;
+      - log2, exp2 and the final operations: 2^-20;
+    with q~ = |qcode| qs (+ |qmean| with Q smoothing) and k~ = |kcode| ks.
+    The FP8 Q/K format adds the row's delta (fp8_score_error).  [B, H, Nq],
+    or [n] for rows."""
+    fmt = codes.get("qk_format", "int8")
+    B, H, Nq, _ = codes["q8"].shape
+    Nkv = codes["k8"].shape[2]
+    nbk = -(-Nkv // 128)
+    dec = ((lambda c: np.abs(oracle.e4m3_decode(c.view(np.uint8)))) if fmt == "fp8"
+           else (lambda c: np.abs(c.astype(np.float64))))
+    out = np.zeros((B, H, Nq)) if rows is None else np.zeros(len(rows))
+    for b in range(B):
+        for h in range(H):
+            if rows is None:
+                qi, sel = np.arange(Nq), None
+            else:
+                sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
+                if sel.size == 0:
+                    continue
+                qi = rows[sel, 2]
+            qt = dec(codes["q8"][b, h, qi]) * codes["q_scale"][b, h][qi // 128].astype(np.float64)[:, None]
+            if "q_mean" in codes:
+                qt = qt + np.abs(codes["q_mean"][b, h][qi // 128].astype(np.float64))
+            kt = dec(codes["k8"][b, h]) * codes["k_scale"][b, h][np.arange(Nkv) // 128].astype(np.float64)[:, None]
+            smag = np.zeros(len(qi))
+            for j0 in range(0, Nkv, 8192):
+                smag = np.maximum(smag, (qt @ np.ascontiguousarray(kt[j0:j0 + 8192].T)).max(axis=1))
+            shift = qt @ np.abs(codes["k_mean"][b, h].astype(np.float64))
+            bar = 2.0 ** -17 * (smag + shift) * scale + (Nkv + 2 * nbk) * 2.0 ** -24 + 2.0 ** -20
+            if sel is None:
+                out[b, h] = bar
+            else:
+                out[sel] = bar
+    if fmt == "fp8":
+        out = out + fp8_score_error(codes, scale, rows)
+    return out

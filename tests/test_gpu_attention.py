@@ -12,7 +12,8 @@ import pytest
 import oracle
 import precision_flash_attention_amd as sattn
 import testkit
-from gpu_helpers import MAX_ERR, MIN_COS, from_dev, log, parity, sample_rows, to_dev, workload
+from gpu_helpers import (FULL_SIZE_STRIDE, MAX_ERR, MIN_COS, from_dev, log, parity, sample_rows_strided, to_dev,
+                         workload)
 
 pytestmark = pytest.mark.gpu
 SCALE = 1.0 / math.sqrt(128.0)
@@ -48,7 +49,7 @@ def test_sampled_rows_full_size(device, cfg_index):
     cfg, q, k, v, codes = workload(cfg_index)
     o = gpu_attention(q, k, v)
     assert not np.any(np.isnan(testkit.bf16_to_f32(o)))
-    rows = sample_rows(cfg.B, cfg.H, cfg.Nq, 12, seed=cfg_index)
+    rows = sample_rows_strided(cfg.B, cfg.H, cfg.Nq, FULL_SIZE_STRIDE[cfg_index], seed=cfg_index)
     want, _, _ = oracle.attention_rows(codes, SCALE, rows)
     got = o[rows[:, 0], rows[:, 2], rows[:, 1]]
     check(got, want, v, f"{cfg.name}, {len(rows)} rows")
@@ -72,32 +73,36 @@ def test_cross_shapes(device, Nq, Nkv):
     check(o, oracle.attention(oracle.quantize(q, k, v), SCALE), v, f"{Nq}x{Nkv}")
 
 
-@pytest.mark.parametrize("scale", [0.01, 0.2])
-def test_softmax_scales(device, scale):
-    log(f"attention softmax_scale={scale}")
-    cfg = testkit.CONFIGS[2]
-    q, k, v = testkit.make_inputs(cfg, H=2, Nq=512, Nkv=512)
+@pytest.mark.parametrize("cfg_index", [2, 4])
+@pytest.mark.parametrize("scale", [0.01, 0.2, 0.5, 1.0])
+def test_softmax_scales(device, cfg_index, scale):
+    # scale 1.0 makes the logits ~11x sharper than the workloads' 1/sqrt(128);
+    # the kernel is held to the same bar against the oracle there (three key
+    # tiles per row, so the online softmax rescales)
+    log(f"attention softmax_scale={scale}, workload {cfg_index} recipe")
+    cfg = testkit.CONFIGS[cfg_index]
+    q, k, v = testkit.make_inputs(cfg, seed=300 + cfg_index, H=2, Nq=384, Nkv=384)
     o = gpu_attention(q, k, v, scale)
     check(o, oracle.attention(oracle.quantize(q, k, v), scale), v, f"scale {scale}")
 
 
-def test_sharp_softmax_is_as_close_to_exact_as_the_oracle(device):
-    # softmax_scale = 1 makes the logits ~11x sharper than any workload; the
-    # INT8 score error then dominates (the oracle itself is ~0.13 max|V| from
-    # exact attention), and the online (running-max) P quantization of the
-    # kernel differs from the oracle's two-pass one by more than the workload
-    # bar.  Both are checked against exact FP64 attention instead.
-    log("attention softmax_scale=1.0 against exact attention")
+def test_sharp_softmax_against_exact_attention(device):
+    # beside the oracle bar: at scale 1.0 the kernel is also no farther from
+    # exact FP64 attention than the oracle (both are dominated by the INT8
+    # score error there)
+    log("attention softmax_scale=1.0 against the oracle and exact attention")
     cfg = testkit.CONFIGS[2]
     q, k, v = testkit.make_inputs(cfg, H=2, Nq=512, Nkv=512)
-    o = testkit.bf16_to_f32(gpu_attention(q, k, v, 1.0)).astype(np.float64).ravel()
-    orc = testkit.bf16_to_f32(oracle.attention(oracle.quantize(q, k, v), 1.0)).astype(np.float64).ravel()
+    ob = gpu_attention(q, k, v, 1.0)
+    orb = oracle.attention(oracle.quantize(q, k, v), 1.0)
+    check(ob, orb, v, "scale 1.0")
+    o = testkit.bf16_to_f32(ob).astype(np.float64).ravel()
+    orc = testkit.bf16_to_f32(orb).astype(np.float64).ravel()
     ref = oracle.bruteforce(q, k, v, 1.0).ravel()
     mv = maxv(v)
     cos = lambda a, b: float(a @ b / np.sqrt((a @ a) * (b @ b)))  # noqa: E731
     e_gpu, e_orc = np.abs(o - ref).max() / mv, np.abs(orc - ref).max() / mv
     log(f"  vs exact: kernel max err {e_gpu:.3e} cos {cos(o, ref):.6f}; oracle {e_orc:.3e} cos {cos(orc, ref):.6f}")
-    assert e_gpu <= 1.25 * e_orc
     assert cos(o, ref) >= cos(orc, ref) - 2e-4
 
 
