@@ -101,8 +101,10 @@ typedef enum { SATTN_QK_INT8 = 0, SATTN_QK_FP8 = 1 } sattn_qk_format;
 /* ABI version of the loaded library (SATTN_ABI_VERSION). */
 int sattn_abi_version(void);
 
-/* Static, human-readable name of a status code. */
-const char* sattn_status_string(sattn_status s);
+/* Static, human-readable name of a status code (a sattn_status value);
+   any other value gives "unknown status".  Taken as int so that an
+   out-of-range value is well defined on both sides of the call. */
+const char* sattn_status_string(int status);
 
 /*
  * Sizes of the two caller-owned device buffers for a problem:

@@ -15,7 +15,8 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# SATTN_ORACLE_LIB: another build of sattn_oracle.c (the sanitizer test's)
+_LIB_PATH = os.environ.get("SATTN_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 _lib = None
 D = 128
 BLK = 128

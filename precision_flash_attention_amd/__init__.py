@@ -49,7 +49,8 @@ __all__ = ["Packed", "SattnError", "QK_FORMATS", "abi_version", "packed_bytes", 
            "fwd_sparse", "unpack_host", "e4m3_encode", "library_path"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "libsattn.so")
+# SATTN_LIBRARY: load another build of the library (the host-sanitizer test's)
+_LIB_PATH = os.environ.get("SATTN_LIBRARY") or os.path.join(HERE, "libsattn.so")
 _lib = None
 
 SATTN_OK = 0

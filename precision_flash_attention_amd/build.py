@@ -3,6 +3,11 @@
 hipcc compiles each translation unit for gfx950 only; quant.hip is built with
 -ffp-contract=off so that every FP32 step of the quantizer is a single IEEE
 operation.  Packed-FP32 VALU instructions are disabled for all device code.
+
+build_host_sanitized(path) builds the same library with AddressSanitizer and
+UndefinedBehaviorSanitizer on the host code only (each -fsanitize after
+-Xarch_host; device code is built as usual), for the CPU test that drives the
+ABI's validation, layout and unpacking paths under the sanitizers.
 """
 import os
 import subprocess
@@ -25,9 +30,14 @@ SOURCES = {
 }
 
 
-def _compile(name: str, extra, verbose: bool) -> str:
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+
+
+def _compile(name: str, extra, verbose: bool, objdir: str = OBJ) -> str:
     src = os.path.join(CSRC, name)
-    obj = os.path.join(OBJ, name + ".o")
+    obj = os.path.join(objdir, name + ".o")
     cmd = [HIPCC] + COMMON + extra + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -50,6 +60,20 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
     return LIB
+
+
+def build_host_sanitized(path: str, verbose: bool = False) -> str:
+    objdir = os.path.join(os.path.dirname(os.path.abspath(path)), "_asan_obj")
+    os.makedirs(objdir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1] + HOST_SANITIZE, verbose, objdir),
+                           SOURCES.items()))
+    cmd = ([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + HOST_SANITIZE
+           + ["-shared-libsan", "-o", path] + objs)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return path
 
 
 if __name__ == "__main__":

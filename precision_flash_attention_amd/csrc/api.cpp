@@ -184,8 +184,8 @@ extern "C" {
 
 int sattn_abi_version(void) { return SATTN_ABI_VERSION; }
 
-const char* sattn_status_string(sattn_status s) {
-  switch (s) {
+const char* sattn_status_string(int status) {
+  switch (status) {
     case SATTN_OK: return "ok";
     case SATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
     case SATTN_ERR_UNSUPPORTED: return "unsupported";

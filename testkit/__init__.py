@@ -18,7 +18,8 @@ from typing import Optional, Tuple
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "libsattn_testkit.so")
+# SATTN_TESTKIT_LIB: another build of sattn_testkit.c (the sanitizer test's)
+_LIB_PATH = os.environ.get("SATTN_TESTKIT_LIB") or os.path.join(HERE, "libsattn_testkit.so")
 _lib = None
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_KBIAS, STREAM_OUTLIER = 1, 2, 3, 4, 5
