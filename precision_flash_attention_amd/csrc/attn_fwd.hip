@@ -120,12 +120,11 @@ __device__ inline void copy_to_lds_off(const uint8_t* src_lane, uint8_t* dst_wav
                                    (void __attribute__((address_space(3)))*)dst_wave, 16, OFF, 0);
 }
 
-// Float whose bits are 0x4B400000 + acc equals 1.5 * 2^23 + acc for
-// |acc| < 2^22; INT8 MFMA accumulators started from these bits can be read
-// as floats without a conversion.
-constexpr int kMagicBits = 0x4B400000;
+// Masked keys of the last tile: the bits of -inf (FP8 Q/K scores are
+// floats) or the integer minimum (INT8 scores, below every score, so the
+// integer row maximum ignores it; the softmax of that tile maps it to -inf).
 constexpr int kNegInfBits = (int)0xFF800000u;
-constexpr float kMagicF = 12582912.0f;
+constexpr int kIntMin = (int)0x80000000u;
 
 // ---------------------------------------------------------------------------
 // 8 waves, 32 queries each.  Waves w and w+4 share a SIMD.
@@ -263,9 +262,6 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     for (int r = 0; r < 16; ++r) O[db][r] = 0.0f;
   v16i S[4];
   uint32_t P[2][8];
-  v16i S0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) S0[r] = kMagicBits;
   float c_cur = 0.0f;       // dequant scale of the tile whose S is held
   bool masked_cur = false;  // block-sparse: that tile is masked for this group
   bool pv_skip = false;     // block-sparse: the P registers belong to a masked tile
@@ -281,9 +277,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   // kst = t % 3, the LDS stage of tile t.  The steady-state loop passes it
   // as a literal, so every LDS address is a lane constant plus an immediate.
   // mask_rem < 128 (the partial last tile only): keys at or past mask_rem
-  // get the bits of -inf.  As an integer that is below every biased score,
-  // so the row maximum ignores it; as a float it gives exp2(fma(-inf, c, nb))
-  // = 0.  The MFMA-issuing wave waits for these S values here, once per sweep.
+  // get the bits of -inf (FP8 Q/K) or the integer minimum (INT8), which the
+  // softmax of that tile turns into p = 0.  The MFMA-issuing wave waits for
+  // these S values here, once per sweep.
   // mask_all (block-sparse): this wave group's query block does not attend
   // tile t.  The group skips the tile's score MFMAs, its V phase and its PV
   // MFMAs (wave-uniform branches): the row maximum, the row sum and O stay
@@ -356,7 +352,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       } else {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], S0, 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], v16i{}, 0, 0, 0);
 #pragma unroll
         for (int m = 1; m < 4; ++m)
 #pragma unroll
@@ -383,18 +379,26 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             asm volatile("" : "+v"(rl));
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rl) S[kb][r] = kNegInfBits;
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= rl) S[kb][r] = FP8QK ? kNegInfBits : kIntMin;
           }
       }
     }
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // INT8 score as a float: the exact conversion of the accumulator; in the
+  // masked last tile the integer minimum stands for -inf
+  auto score_f = [&](int s, bool masked) __attribute__((always_inline)) -> float {
+    if constexpr (FP8QK) return __int_as_float(s);
+    else return masked && s == kIntMin ? -__builtin_inff() : (float)s;
+  };
+
   // ---- V(t): online softmax of S -> P, conditional rescale of O
   // first: the sweep's first tile (m = -inf, O = 0 and l = 0 before it), where
   // the rescale would multiply zeros by exp2(-inf); the block-sparse instance
-  // keeps it, since its first attended tile depends on the table
-  auto vblock = [&](bool first) __attribute__((always_inline)) {
+  // keeps it, since its first attended tile depends on the table.
+  // masked: the tile holds keys past Nkv (the sweep's last tile only).
+  auto vblock = [&](bool first, bool masked) __attribute__((always_inline)) {
     if constexpr (SPARSE) {
       pv_skip = masked_cur;
       if (masked_cur) return;
@@ -408,9 +412,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     if constexpr (QSMOOTH) {
       // add Delta-S (in the units of S: the table holds (qmean . kcode) / qs)
       // of this group's query block to every score, written back over S,
-      // then the row maximum on floats; masked keys stay -inf.  For INT8 the
-      // accumulator's bias is taken off first (exact: both are integers
-      // below 2^24), so the sum is rounded at the score's own magnitude.
+      // then the row maximum on floats; masked keys become -inf.  The INT8
+      // accumulator is converted exactly first, so the sum is rounded once,
+      // at the score's own magnitude.
       const float* dsl = reinterpret_cast<const float*>(smem + dstage_cur * kStage + 2 * kTileBytes) +
                          (isA ? 0 : 128) + 4 * hh;
       float mx = -__builtin_inff();
@@ -423,8 +427,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
           for (int b2 = 0; b2 < 4; ++b2) {
             const int r = 4 * a + b2;
-            const float sv = FP8QK ? __int_as_float(S[kb][r]) : __int_as_float(S[kb][r]) - kMagicF;
-            const float tt = sv + dv[b2];
+            const float tt = score_f(S[kb][r], masked) + dv[b2];
             S[kb][r] = __float_as_int(tt);
             mx = fmaxf(mx, tt);
           }
@@ -441,13 +444,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       mx = fmaxf(mx, other_half_f(mx));
       mt = mx * c;
     } else {
-      int mx = 0x4B000000;  // the bits of 2^23: below every biased score
+      int mx = kIntMin;  // masked keys hold the minimum; every tile has a valid key
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = max(mx, (int)S[kb][r]);
       mx = max(mx, other_half_i(mx));
-      mt = (__int_as_float(mx) - kMagicF) * c;
+      mt = (float)mx * c;
     }
     const float mnew = fmaxf(m_run, mt);
     if (!(first && !SPARSE) && __any(mnew > m_run)) {
@@ -460,12 +463,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     }
     m_run = mnew;
     // exponent argument fma(s, c, nb) = (score - m) log2 e + log2 448 with
-    // nb = log2 448 - m, rounded once.  For INT8 codes the float view of S
-    // carries the bias 1.5 * 2^23; it is subtracted from each score (exact)
-    // rather than folded into nb, because nb - 1.5 * 2^23 c would be rounded
-    // at the magnitude of 1.5 * 2^23 c: a per-tile shift of the reference
-    // point that moves P's E4M3 rounding and reweights a row's tiles, by
-    // more than the accuracy bar at sharp softmax scales.
+    // nb = log2 448 - m, rounded once, s the exact float value of the INT8
+    // accumulator (one conversion per score).  Reading the accumulators as
+    // floats through a bias 1.5 * 2^23 in their initial value, and folding
+    // that bias into nb, would save the conversion but round nb at the
+    // magnitude of 1.5 * 2^23 c: a per-tile shift of the reference point that
+    // moves P's E4M3 rounding and reweights a row's tiles, by more than the
+    // accuracy bar at sharp softmax scales.
     const float nb = kLog2_448 - mnew;
     float ls[4];
 #pragma unroll
@@ -477,8 +481,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sf = __int_as_float(S[kb][r0 + i]);
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(FP8QK || QSMOOTH ? sf : sf - kMagicF, c, nb));
+          const float sf = QSMOOTH ? __int_as_float(S[kb][r0 + i]) : score_f(S[kb][r0 + i], masked);
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sf, c, nb));
           // the first term starts the sum (p >= 0, so 0 + p == p)
           ls[i] = (g == 0 && j == 0) ? pv[i] : ls[i] + pv[i];
         }
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   auto step = [&](int t, bool do_pv, int kst) __attribute__((always_inline)) {
     mblock(t, do_pv, true, kst, 128, SPARSE && !group_attends(t));
     barrier();
-    vblock(!do_pv);
+    vblock(!do_pv, false);
     if (isA) wait_loads();
     barrier();
   };
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   for (; t < last; ++t) step(t, true, t % 3);
   mblock(last, last > 0, true, last % 3, rem, SPARSE && !group_attends(last));
   barrier();
-  vblock(last == 0);
+  vblock(last == 0, rem < 128);
   if (isA) wait_loads();
   barrier();
   mblock(nbk, true, false, nbk % 3, 128, false);
@@ -793,12 +797,18 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_pp_kernel<FP8QK, SPARSE, QSMOOTH>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  CombP c{p.opart, p.lpart, p.out, p.lse, p.os0, p.os1, p.os2, p.BH * L.Nq, p.H, p.Nq, p.splits};
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((c.rows + 7) / 8)), dim3(256), 0, stream, c);
-  return hipGetLastError();
+  return launch_combine(p.opart, p.lpart, a, stream);
 }
 
 }  // namespace
+
+hipError_t launch_combine(const float* opart, const float* lpart, const AttnArgs& a, hipStream_t stream) {
+  const int64_t BH = a.L.B * a.L.H;
+  CombP c{opart, lpart, a.out, a.lse, a.o_str[0], a.o_str[1], a.o_str[2], BH * a.L.Nq, (int)a.L.H,
+          (int)a.L.Nq, a.splits};
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((c.rows + 7) / 8)), dim3(256), 0, stream, c);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
   (void)cross;

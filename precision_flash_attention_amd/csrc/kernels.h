@@ -54,6 +54,8 @@ inline int64_t split_workspace_bytes(int64_t splits, int64_t bh, int64_t nq) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream);
+// merge of split-KV partials (FP32 outputs and LSE) into out and lse
+hipError_t launch_combine(const float* opart, const float* lpart, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
 hipError_t launch_block_lut(const uint8_t* mask, const Layout& L, uint8_t* lut, hipStream_t stream);
 

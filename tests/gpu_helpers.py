@@ -101,9 +101,9 @@ def sample_rows_strided(B: int, H: int, Nq: int, stride: int, seed: int) -> np.n
 
 
 # rows per sample group at full size: every wave of the Wan-like and
-# cross-attention workloads, every other wave of the long-sequence one
-# (whose rows cost twice as much in the oracle)
-FULL_SIZE_STRIDE = {3: 32, 4: 32, 5: 64}
+# cross-attention workloads; on the long-sequence one (whose oracle rows
+# cost twice as much) one row in every 128, i.e. every query block
+FULL_SIZE_STRIDE = {3: 32, 4: 32, 5: 128}
 
 
 # FP8 Q/K format: v_mfma_scale_f32_32x32x64_f8f6f4 does not return the
