@@ -63,6 +63,9 @@ extern "C" {
 #define SATTN_MAX_BLOCKS (1 << 22)
 /* largest num_splits of the split-KV forward calls */
 #define SATTN_MAX_SPLITS 256
+/* Size of the static workspace of sattn_quantize_qkv_noalloc (16 MiB per
+   device; enough for B*H*ceil(Nkv/128) <= 16384). */
+#define SATTN_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
 
 typedef enum {
   SATTN_OK = 0,
@@ -193,6 +196,25 @@ sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
                                    const int64_t* v_strides, int qk_format,
                                    void* packed, size_t packed_bytes,
                                    void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * sattn_quantize_qkv_ex without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving
+ * loops and harnesses that forbid allocation): the per-block K sums and V
+ * maxima go to a static device array of SATTN_NOALLOC_WORKSPACE_BYTES, one
+ * per GPU, held by the library until the process ends.  The call allocates
+ * nothing; the caller still passes inputs and `packed`.  Results are those
+ * of sattn_quantize_qkv_ex bit for bit.
+ * Errors as sattn_quantize_qkv_ex, plus SATTN_ERR_UNSUPPORTED when the
+ * problem's workspace (sattn_packed_bytes) exceeds the static array, and
+ * SATTN_ERR_DEVICE when its device address cannot be obtained.  Every call
+ * on one GPU uses the same array: calls that overlap on a GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+sattn_status sattn_quantize_qkv_noalloc(const void* q, const void* k, const void* v,
+                                        int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                        const int64_t* q_strides, const int64_t* k_strides,
+                                        const int64_t* v_strides, int qk_format,
+                                        void* packed, size_t packed_bytes, void* stream);
 sattn_status sattn_fwd_ex(const void* packed, size_t packed_bytes, int qk_format,
                           int64_t B, int64_t H, int64_t N, int64_t D, float softmax_scale,
                           void* out, const int64_t* out_strides, float* lse, int num_splits,

@@ -44,7 +44,8 @@ from typing import Dict, Optional, Tuple
 
 import torch
 
-__all__ = ["Packed", "SattnError", "QK_FORMATS", "abi_version", "packed_bytes", "quantize_qkv", "fwd",
+__all__ = ["Packed", "SattnError", "QK_FORMATS", "abi_version", "packed_bytes", "quantize_qkv",
+           "quantize_qkv_noalloc", "fwd",
            "fwd_cross", "attention", "fwd_workspace_bytes", "BlockLut", "block_lut_bytes", "block_lut",
            "fwd_sparse", "unpack_host", "e4m3_encode", "library_path"]
 
@@ -93,6 +94,8 @@ def _load():
         lib.sattn_quantize_qkv.argtypes = [_P, _P, _P] + [_I64] * 5 + [_I64P] * 3 + [_P, _SZ, _P, _SZ, _P]
         lib.sattn_fwd.argtypes = [_P, _SZ] + [_I64] * 4 + [ctypes.c_float, _P, _I64P, _P]
         lib.sattn_fwd_cross.argtypes = [_P, _SZ] + [_I64] * 5 + [ctypes.c_float, _P, _I64P, _P]
+        lib.sattn_quantize_qkv_noalloc.argtypes = ([_P, _P, _P] + [_I64] * 5 + [_I64P] * 3 + [ctypes.c_int]
+                                                   + [_P, _SZ, _P])
         lib.sattn_quantize_qkv_ex.argtypes = ([_P, _P, _P] + [_I64] * 5 + [_I64P] * 3 + [ctypes.c_int]
                                               + [_P, _SZ, _P, _SZ, _P])
         lib.sattn_fwd_ex.argtypes = ([_P, _SZ, ctypes.c_int] + [_I64] * 4
@@ -214,6 +217,28 @@ def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                          packed.numel() * packed.element_size(), workspace.data_ptr(),
                                          workspace.numel() * workspace.element_size(),
                                          _stream_ptr(q4.device)), "sattn_quantize_qkv")
+    return Packed(packed, B, H, Nq, Nkv, sq, qk_format, q_smooth)
+
+
+def quantize_qkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, packed: torch.Tensor,
+                         qk_format: str = "int8", q_smooth: bool = False) -> Packed:
+    """As quantize_qkv into the caller's `packed` (uint8, packed_bytes long),
+    with the library's static device workspace instead of a caller's
+    (sattn_quantize_qkv_noalloc): nothing is allocated.  Calls that overlap
+    on one GPU share that workspace and race."""
+    fmt = _format(qk_format, q_smooth)
+    q4, sq = _as4d(q, "q")
+    k4, _ = _as4d(k, "k")
+    v4, _ = _as4d(v, "v")
+    B, Nq, H, D = q4.shape
+    Nkv = k4.shape[1]
+    if tuple(k4.shape) != (B, Nkv, H, D) or tuple(v4.shape) != (B, Nkv, H, D):
+        raise ValueError(f"shape mismatch: q {tuple(q4.shape)} k {tuple(k4.shape)} v {tuple(v4.shape)}")
+    qs, ks, vs = _strides(q4), _strides(k4), _strides(v4)
+    _check(_load().sattn_quantize_qkv_noalloc(q4.data_ptr(), k4.data_ptr(), v4.data_ptr(), B, H, Nq, Nkv, D,
+                                              qs, ks, vs, fmt, packed.data_ptr(),
+                                              packed.numel() * packed.element_size(), _stream_ptr(q4.device)),
+           "sattn_quantize_qkv_noalloc")
     return Packed(packed, B, H, Nq, Nkv, sq, qk_format, q_smooth)
 
 

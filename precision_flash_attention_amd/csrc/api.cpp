@@ -213,35 +213,66 @@ sattn_status sattn_packed_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, i
   return sattn_packed_bytes_ex(B, H, Nq, Nkv, D, SATTN_QK_INT8, packed_bytes, workspace_bytes);
 }
 
-sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
-                                   int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
-                                   const int64_t* q_strides, const int64_t* k_strides,
-                                   const int64_t* v_strides, int qk_format,
-                                   void* packed, size_t packed_bytes,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the quantize entry points.  workspace == nullptr with
+// use_static: the library's static workspace (sattn_quantize_qkv_noalloc).
+sattn_status quantize_common(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t Nq,
+                             int64_t Nkv, int64_t D, const int64_t* q_strides, const int64_t* k_strides,
+                             const int64_t* v_strides, int qk_format, void* packed, size_t packed_bytes,
+                             void* workspace, size_t workspace_bytes, bool use_static, void* stream) {
   sattn_status s = check_dims(B, H, Nq, Nkv, D);
   if (s != SATTN_OK) return s;
   if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
   if ((s = check_qsmooth(B, H, Nq, Nkv, qk_format)) != SATTN_OK) return s;
-  if (!q || !k || !v || !packed || !workspace) return SATTN_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(packed) || !aligned16(workspace))
+  if (!q || !k || !v || !packed || (!use_static && !workspace)) return SATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(packed) ||
+      (!use_static && !aligned16(workspace)))
     return SATTN_ERR_INVALID_ARGUMENT;
   sattn::QuantArgs a;
   if ((s = get_strides(q_strides, Nq, H, a.q_str)) != SATTN_OK) return s;
   if ((s = get_strides(k_strides, Nkv, H, a.k_str)) != SATTN_OK) return s;
   if ((s = get_strides(v_strides, Nkv, H, a.v_str)) != SATTN_OK) return s;
   a.L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format));
-  if (packed_bytes < a.L.packed_bytes || workspace_bytes < a.L.workspace_bytes)
-    return SATTN_ERR_BUFFER_TOO_SMALL;
+  if (packed_bytes < a.L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
+  if (use_static ? a.L.workspace_bytes > SATTN_NOALLOC_WORKSPACE_BYTES : workspace_bytes < a.L.workspace_bytes)
+    return use_static ? SATTN_ERR_UNSUPPORTED : SATTN_ERR_BUFFER_TOO_SMALL;
   s = check_device();
   if (s != SATTN_OK) return s;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (use_static && sattn::noalloc_workspace(&ws) != hipSuccess) return SATTN_ERR_DEVICE;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.packed = static_cast<uint8_t*>(packed);
-  a.workspace = static_cast<uint8_t*>(workspace);
+  a.workspace = ws;
   a.fp8qk = is_fp8(qk_format);
   return launch_status(sattn::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+sattn_status sattn_quantize_qkv_ex(const void* q, const void* k, const void* v,
+                                   int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                   const int64_t* q_strides, const int64_t* k_strides,
+                                   const int64_t* v_strides, int qk_format,
+                                   void* packed, size_t packed_bytes,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_common(q, k, v, B, H, Nq, Nkv, D, q_strides, k_strides, v_strides, qk_format, packed,
+                         packed_bytes, workspace, workspace_bytes, false, stream);
+}
+
+sattn_status sattn_quantize_qkv_noalloc(const void* q, const void* k, const void* v,
+                                        int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                                        const int64_t* q_strides, const int64_t* k_strides,
+                                        const int64_t* v_strides, int qk_format,
+                                        void* packed, size_t packed_bytes, void* stream) {
+  return quantize_common(q, k, v, B, H, Nq, Nkv, D, q_strides, k_strides, v_strides, qk_format, packed,
+                         packed_bytes, nullptr, 0, true, stream);
 }
 
 sattn_status sattn_quantize_qkv(const void* q, const void* k, const void* v,

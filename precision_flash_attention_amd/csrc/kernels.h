@@ -53,6 +53,10 @@ inline int64_t split_workspace_bytes(int64_t splits, int64_t bh, int64_t nq) {
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// Size and device address (on the current device) of the static workspace
+// that sattn_quantize_qkv_noalloc uses instead of a caller's.
+constexpr size_t kNoallocWorkspaceBytes = (size_t)16 << 20;
+hipError_t noalloc_workspace(uint8_t** out);
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream);
 // merge of split-KV partials (FP32 outputs and LSE) into out and lse
 hipError_t launch_combine(const float* opart, const float* lpart, const AttnArgs& a, hipStream_t stream);

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "layout.h"
 
@@ -583,6 +585,34 @@ __global__ __launch_bounds__(256) void k_e4m3(const float* x, uint8_t* out, int6
 }
 
 }  // namespace
+
+// Workspace of sattn_quantize_qkv_noalloc, for callers that cannot allocate:
+// a file-scope device array (one per GPU, held until the process ends) in
+// place of the caller's workspace.  Its contents need no clearing: the
+// statistics kernels write every partial before anything reads it.  Calls
+// that overlap on one GPU share it and race.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoallocWorkspaceBytes];
+
+hipError_t noalloc_workspace(uint8_t** out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<uint8_t*> addr[kMaxDev];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  uint8_t* ptr = addr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    // the array's name is a host-side stand-in: its device address comes
+    // from the runtime, once per device, with that device current
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr = static_cast<uint8_t*>(a);
+    addr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
