@@ -26,6 +26,7 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950", "-fno-gpu-flush
 SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "attn_fwd.hip": [],
+    "attn_short.hip": [],
     "api.cpp": ["-x", "hip"],
 }
 

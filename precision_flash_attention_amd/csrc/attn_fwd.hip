@@ -816,6 +816,7 @@ hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream) {
     return a.fp8qk ? launch_pp<true, true, false>(a, stream) : launch_pp<false, true, false>(a, stream);
   if (a.L.qsmooth)
     return a.fp8qk ? launch_pp<true, false, true>(a, stream) : launch_pp<false, false, true>(a, stream);
+  if (short_kv_applies(a)) return launch_attention_short(a, stream);
   return a.fp8qk ? launch_pp<true, false, false>(a, stream) : launch_pp<false, false, false>(a, stream);
 }
 

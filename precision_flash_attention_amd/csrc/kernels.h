@@ -58,6 +58,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 constexpr size_t kNoallocWorkspaceBytes = (size_t)16 << 20;
 hipError_t noalloc_workspace(uint8_t** out);
 hipError_t launch_attention(const AttnArgs& a, bool cross, hipStream_t stream);
+// short key sequences (at most four 128-key tiles), many query tiles, no
+// split, dense: persistent workgroups with the head's K/V resident in LDS
+bool short_kv_applies(const AttnArgs& a);
+hipError_t launch_attention_short(const AttnArgs& a, hipStream_t stream);
 // merge of split-KV partials (FP32 outputs and LSE) into out and lse
 hipError_t launch_combine(const float* opart, const float* lpart, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
