@@ -40,11 +40,18 @@ METRIC = "attention TFLOP/s (4·B·H·Nq·Nkv·D), INT8-QK/FP8-PV, D=128; % of M
 PEAK_TFLOPS = 5000.0     # MI355X dense INT8 / FP8 MFMA
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
 ATTN_KERNEL = "attn_pp_kernel"
-# Sources that fix the attention kernel's code; the committed traffic record
+SHORT_KERNEL = "attn_short_kernel"
+# Sources that fix each attention kernel's code; a committed traffic record
 # is used only while their digest matches the one it was measured with.
-ATTN_SOURCES = ("precision_flash_attention_amd/csrc/attn_fwd.hip",
-                "precision_flash_attention_amd/csrc/layout.h",
-                "precision_flash_attention_amd/csrc/kernels.h")
+KERNEL_SOURCES = {
+    ATTN_KERNEL: ("precision_flash_attention_amd/csrc/attn_fwd.hip",
+                  "precision_flash_attention_amd/csrc/layout.h",
+                  "precision_flash_attention_amd/csrc/kernels.h"),
+    SHORT_KERNEL: ("precision_flash_attention_amd/csrc/attn_short.hip",
+                   "precision_flash_attention_amd/csrc/layout.h",
+                   "precision_flash_attention_amd/csrc/kernels.h"),
+}
+ATTN_SOURCES = KERNEL_SOURCES[ATTN_KERNEL]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_pp_kernel_wan_b1h40n32760_traffic.md")
 COPY_BYTES = 1 << 30
 
@@ -60,33 +67,55 @@ def quant_unique_bytes(B, H, Nq, Nkv):
     return B * H * 128 * (Nq + 2 * Nkv) * 3
 
 
-def attn_kernel_digest():
+def attn_kernel_digest(kernel=ATTN_KERNEL):
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, qk_format):
-    """HBM bytes per attention launch from the committed FETCH_SIZE and
+def traffic_records():
+    """Every traffic record committed under profiles/ (lines starting with
+    'traffic-record: ' in the *_traffic.md summaries)."""
+    import glob
+    recs = []
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        with open(path) as fh:
+            recs += [json.loads(ln[len("traffic-record: "):]) for ln in fh if ln.startswith("traffic-record: ")]
+    return recs
+
+
+def measured_traffic(workload, qk_format, kernel=ATTN_KERNEL):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE and
     WRITE_SIZE passes, each scaled by what the same counter read for a plain
-    device copy of COPY_BYTES; None when there is no record for this workload
-    or the kernel sources changed since it was taken."""
-    try:
-        with open(TRAFFIC_RECORD) as fh:
-            recs = [json.loads(ln[len("traffic-record: "):]) for ln in fh if ln.startswith("traffic-record: ")]
-    except OSError:
-        return None
-    digest = attn_kernel_digest()
-    recs = [r for r in recs if r.get("kernel_digest") == digest and r.get("workload") == workload
-            and r.get("qk_format", "int8") == qk_format]
+    device copy of COPY_BYTES; None when there is no record for this kernel
+    and workload or the kernel's sources changed since it was taken."""
+    recs = traffic_records()
+    digest = attn_kernel_digest(kernel)
+    recs = [r for r in recs if r.get("kernel", ATTN_KERNEL) == kernel and r.get("kernel_digest") == digest
+            and r.get("workload") == workload and r.get("qk_format", "int8") == qk_format]
     if not recs:
         return None
     rec = recs[0]
     fetch = rec["fetch_kib"] * rec["copy_bytes"] / rec["copy_fetch_kib"]
     write = rec["write_kib"] * rec["copy_bytes"] / rec["copy_write_kib"]
     return int(round(fetch + write))
+
+
+def attention_kernel(B, H, Nq, Nkv, cus, sparse=False, q_smooth=False, splits=1, out_row_stride=None):
+    """The kernel the library runs for a forward call of this shape: the
+    short-KV kernel for 1-4 key tiles and more 256-query tiles than CUs
+    (no block mask, no Q smoothing, one split, output rows 128 to 2^24
+    elements apart), else attn_pp_kernel.  Mirrors the library's dispatch
+    rule, for naming the kernel the roofline describes."""
+    nbk = -(-Nkv // 128)
+    os1 = H * 128 if out_row_stride is None else out_row_stride
+    tiles = B * H * (-(-Nq // 256))
+    if (not sparse and not q_smooth and splits == 1 and 1 <= nbk <= 4 and 128 <= os1 < (1 << 24)
+            and cus < tiles < (1 << 30)):
+        return SHORT_KERNEL
+    return ATTN_KERNEL
 
 
 PEAK_SCLK_MHZ = 2400.0    # the clock the 5.0 PFLOP/s peak is quoted at
@@ -282,6 +311,8 @@ def main():
     t_attn_min = min(e[1].elapsed_time(e[2]) for e in events)
     t_attn_med = sorted(e[1].elapsed_time(e[2]) for e in events)[len(events) // 2]
 
+    kernel = attention_kernel(cfg.B, cfg.H, cfg.Nq, cfg.Nkv, torch.cuda.get_device_properties(0).multi_processor_count,
+                              sparse=sparse, q_smooth=args.q_smooth, splits=splits)
     flops = cfg.flops
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tf = flops / (t_attn * 1e-3) / 1e12
@@ -316,11 +347,11 @@ def main():
                      "gbs": round(qbytes / (t_quant * 1e-3) / 1e9, 1),
                      "frac_of_hbm_peak": round(qbytes / (t_quant * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "gpu_clock": clock,
-        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": round(attn_tf, 2),
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(attn_tf, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(cfg.name, args.qk_format),
+                     "traffic": measured_traffic(cfg.name, args.qk_format, kernel),
                      "algo_bytes": attn_algo_bytes(cfg.B, cfg.H, cfg.Nq, cfg.Nkv),
-                     "kernel_digest": attn_kernel_digest()},
+                     "kernel_digest": attn_kernel_digest(kernel)},
     }
     if args.copy_calibration:
         copy_calibration(torch, dev)

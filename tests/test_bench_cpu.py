@@ -27,6 +27,27 @@ def _records():
         return [json.loads(ln[len("traffic-record: "):]) for ln in fh if ln.startswith("traffic-record: ")]
 
 
+def test_every_profile_record_is_read():
+    recs = bench.traffic_records()
+    assert all(r in recs for r in _records())
+    assert all(r.get("kernel", bench.ATTN_KERNEL) in bench.KERNEL_SOURCES for r in recs)
+
+
+def test_kernel_named_by_the_dispatch_rule():
+    k = bench.attention_kernel
+    # text cross-attention: 4 key tiles, 10240 query tiles on 256 CUs
+    assert k(2, 40, 32760, 512, 256) == bench.SHORT_KERNEL
+    assert k(2, 40, 32760, 513, 256) == bench.ATTN_KERNEL      # 5 key tiles
+    assert k(1, 40, 32760, 32760, 256) == bench.ATTN_KERNEL    # Wan-like
+    assert k(1, 2, 256, 256, 256) == bench.ATTN_KERNEL         # 2 query tiles
+    assert k(1, 1, 256 * 256, 1, 256) == bench.ATTN_KERNEL     # exactly one tile per CU
+    assert k(1, 1, 256 * 257, 1, 256) == bench.SHORT_KERNEL
+    assert k(2, 40, 32760, 512, 256, sparse=True) == bench.ATTN_KERNEL
+    assert k(2, 40, 32760, 512, 256, q_smooth=True) == bench.ATTN_KERNEL
+    assert k(2, 40, 32760, 512, 256, splits=2) == bench.ATTN_KERNEL
+    assert k(2, 40, 32760, 512, 256, out_row_stride=64) == bench.ATTN_KERNEL
+
+
 def test_traffic_record_is_reported_only_for_its_kernel():
     recs = [r for r in _records() if r["workload"] == WAN]
     assert {r["qk_format"] for r in recs} == {"int8", "fp8"}
@@ -48,7 +69,8 @@ def test_traffic_record_is_reported_only_for_its_kernel():
 
 def test_traffic_is_null_for_other_kernels_and_workloads(monkeypatch):
     assert bench.measured_traffic("text cross-attention", "int8") is None
-    monkeypatch.setattr(bench, "attn_kernel_digest", lambda: "0" * 16)
+    assert bench.measured_traffic(WAN, "int8", bench.SHORT_KERNEL) is None
+    monkeypatch.setattr(bench, "attn_kernel_digest", lambda kernel=bench.ATTN_KERNEL: "0" * 16)
     assert bench.measured_traffic(WAN, "int8") is None
 
 
