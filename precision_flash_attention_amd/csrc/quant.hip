@@ -327,10 +327,27 @@ __device__ inline uint32_t e4m3_code(float v, float s, float r, bool exact) {
   return e4m3_hw(clamp448(__fdiv_rn(v, s)));
 }
 
+// x from another lane under a DPP control (all rows and banks enabled)
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the wave, in every lane, without LDS: DPP within each row of
+// 16 lanes (quad permutations, then rotations by 4 and 8), then the row
+// swaps of gfx950 (v_permlane16_swap, v_permlane32_swap) across rows.
+// A maximum is exact, so the order does not change the result.
 __device__ inline float wave_max(float a) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-  return a;
+  a = fmaxf(a, dpp_f<0xB1>(a));   // quad_perm [1, 0, 3, 2]
+  a = fmaxf(a, dpp_f<0x4E>(a));   // quad_perm [2, 3, 0, 1]
+  a = fmaxf(a, dpp_f<0x124>(a));  // row_ror:4
+  a = fmaxf(a, dpp_f<0x128>(a));  // row_ror:8
+  const int x = __float_as_int(a);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  a = fmaxf(__int_as_float((int)r16[0]), __int_as_float((int)r16[1]));
+  const int y = __float_as_int(a);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__int_as_float((int)r32[0]), __int_as_float((int)r32[1]));
 }
 
 struct CodeP {
