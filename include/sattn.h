@@ -95,9 +95,16 @@ typedef enum { SATTN_QK_INT8 = 0, SATTN_QK_FP8 = 1 } sattn_qk_format;
  * block's tokens (token order, one division by their count) is subtracted
  * before the block is coded, and every score gets back Delta-S = ks(j) *
  * (q_mean . kcode_j) * softmax_scale.  The packed buffer then also holds the
- * means and a Delta-S table of B*H*ceil(Nq/128)*ceil(Nkv/128)*128 floats
- * (size from sattn_packed_bytes_ex); the quantize call runs two more kernels
- * and the forward one more addition per score.  Not with sattn_fwd_sparse.
+ * means (size from sattn_packed_bytes_ex) and:
+ *   - with SATTN_QK_INT8, per Q block four int8 digit rows of the mean in
+ *     the block's score unit and 8 parameters (512 + 32 bytes); the forward
+ *     forms Delta-S on the INT8 MFMA from them, rounded to the score unit
+ *     (qs; a coarser unit qs * 2^k, with the block's Q codes rounded to it,
+ *     only where the mean exceeds 2^15 code units), as the initial value of
+ *     the score accumulators;
+ *   - with SATTN_QK_FP8, a Delta-S table of B*H*ceil(Nq/128)*ceil(Nkv/128)*
+ *     128 floats, added to each score by the forward.
+ * Not with sattn_fwd_sparse.
  */
 #define SATTN_QK_SMOOTH_Q 0x10
 

@@ -91,7 +91,7 @@ bool is_qsmooth(int f) { return (f & SATTN_QK_SMOOTH_Q) != 0; }
 // Q smoothing adds a Delta-S table of B*H*nbq*nbk*128 floats; past 2^40
 // bytes (far beyond device memory) the sizes are refused.
 sattn_status check_qsmooth(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int f) {
-  if (!is_qsmooth(f)) return SATTN_OK;
+  if (!is_qsmooth(f) || !is_fp8(f)) return SATTN_OK;
   const double bytes = (double)B * (double)H * (double)sattn::nblocks(Nq) * (double)sattn::nblocks(Nkv) * 512.0;
   return bytes > 1099511627776.0 ? SATTN_ERR_UNSUPPORTED : SATTN_OK;
 }
@@ -155,7 +155,7 @@ sattn_status fwd_common(const void* packed, size_t packed_bytes, int qk_format, 
   sattn::AttnArgs a;
   s = get_strides(out_strides, Nq, H, a.o_str);
   if (s != SATTN_OK) return s;
-  a.L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format));
+  a.L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format), is_fp8(qk_format));
   if (packed_bytes < a.L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
   s = check_device();
   if (s != SATTN_OK) return s;
@@ -202,7 +202,7 @@ sattn_status sattn_packed_bytes_ex(int64_t B, int64_t H, int64_t Nq, int64_t Nkv
   if (s != SATTN_OK) return s;
   if (!valid_format(qk_format)) return SATTN_ERR_INVALID_ARGUMENT;
   if ((s = check_qsmooth(B, H, Nq, Nkv, qk_format)) != SATTN_OK) return s;
-  const Layout L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format));
+  const Layout L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format), is_fp8(qk_format));
   if (packed_bytes) *packed_bytes = L.packed_bytes;
   if (workspace_bytes) *workspace_bytes = L.workspace_bytes;
   return SATTN_OK;
@@ -235,7 +235,7 @@ sattn_status quantize_common(const void* q, const void* k, const void* v, int64_
   if ((s = get_strides(q_strides, Nq, H, a.q_str)) != SATTN_OK) return s;
   if ((s = get_strides(k_strides, Nkv, H, a.k_str)) != SATTN_OK) return s;
   if ((s = get_strides(v_strides, Nkv, H, a.v_str)) != SATTN_OK) return s;
-  a.L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format));
+  a.L = sattn::make_layout(B, H, Nq, Nkv, is_qsmooth(qk_format), is_fp8(qk_format));
   if (packed_bytes < a.L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
   if (use_static ? a.L.workspace_bytes > SATTN_NOALLOC_WORKSPACE_BYTES : workspace_bytes < a.L.workspace_bytes)
     return use_static ? SATTN_ERR_UNSUPPORTED : SATTN_ERR_BUFFER_TOO_SMALL;
@@ -402,8 +402,9 @@ sattn_status sattn_unpack_q_mean_host(const void* packed_host, size_t packed_byt
   if ((s = check_qsmooth(B, H, Nq, Nkv, SATTN_QK_SMOOTH_Q)) != SATTN_OK) return s;
   if (packed_host == nullptr || q_mean == nullptr) return SATTN_ERR_INVALID_ARGUMENT;
   const Layout L = sattn::make_layout(B, H, Nq, Nkv, true);
-  if (packed_bytes < L.packed_bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
-  memcpy(q_mean, static_cast<const uint8_t*>(packed_host) + L.off_qm, (size_t)(B * H * L.nbq) * 128 * 4);
+  const size_t bytes = (size_t)(B * H * L.nbq) * 128 * 4;
+  if (packed_bytes < L.off_qm + bytes) return SATTN_ERR_BUFFER_TOO_SMALL;
+  memcpy(q_mean, static_cast<const uint8_t*>(packed_host) + L.off_qm, bytes);
   return SATTN_OK;
 }
 

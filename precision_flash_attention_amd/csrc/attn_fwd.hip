@@ -77,8 +77,10 @@ struct AttnP {
   float* lpart;  //   and their LSE [splits][B*H][Nq]
   const int32_t* lut_counts;    // block-sparse: key tiles per query tile [B*H*mt]
   const uint32_t* lut_entries;  //   and their entries [B*H*mt][nbk]
-  const float* ds;              // Q smoothing: Delta-S [B*H][nbq][nbk*128]
-  const float* qm;              //   and the Q block means [B*H][nbq][128]
+  const float* ds;              // Q smoothing, E4M3 codes: Delta-S [B*H][nbq][nbk*128]
+  const int8_t* dg;             //   INT8 codes: digit rows of mean / unit [B*H][nbq][4][128]
+  const float* dp;              //   and their parameters [B*H][nbq][8]
+  const float* qm;              //   the Q block means [B*H][nbq][128]
   int64_t G;     // logical workgroups: B*H*splits*mt
   int64_t BH;
   int H, Nq, Nkv, nbq, nbk, mt;
@@ -137,18 +139,36 @@ constexpr int kIntMin = (int)0x80000000u;
 // M(t) = O += V(t-1)^T . P(t-1) followed by S(t) = K(t) . Q^T;
 // V(t) = online softmax of S(t) -> P(t), with the conditional O rescale.
 // Tile u lives in LDS stage u % 3 from slot 2u (K read by A) to slot 2u+3
-// (V read by B); group A loads tile t+1 at the start of M(t) and waits for
-// it at the end of V(t).
+// (V read by B).  Tile t+1 is loaded in halves: its K tile by group A at the
+// start of A's M(t), waited for at the end of A's V(t); its V^T tile by
+// group B at the start of B's M(t), waited for at the end of B's V(t).
+// (INT8 Q smoothing: four stages, tile t+2 loaded in M(t), whose waves also
+// form Delta-S of tile t+1.)
 // FP8QK: Q and K codes are E4M3 (the FP8/FP8/BF16 format): S^T comes from
 // v_mfma_scale_f32_32x32x64_f8f6f4 in FP32, the K operands being the same
 // LDS reads taken two 16-byte chunks per MFMA.
 // QSMOOTH: Q was smoothed per block; each score gets the Delta-S term of its
-// query block and key, staged with the tile (1 KiB: the two query blocks'
-// 128 values) in LDS.
+// query block and key.  INT8 codes: the wave forms it in its MFMA phase from
+// the block's digit rows and the K operands it already holds (16 more INT8
+// MFMAs), rounds it to the accumulator unit and starts the score
+// accumulators from it, so the softmax phase is the unsmoothed one.  E4M3
+// codes: a table staged with the tile (1 KiB: the two query blocks' 128
+// values) in LDS, added to each score in the softmax phase.
 template <bool FP8QK, bool SPARSE, bool QSMOOTH>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int kStage = kStageBytes + (QSMOOTH ? 1024 : 0);
+  constexpr bool DS_MFMA = QSMOOTH && !FP8QK;   // Delta-S from digit rows, in the accumulator
+  constexpr bool DS_TABLE = QSMOOTH && FP8QK;   // Delta-S from the table, added per score
+  constexpr int kStage = kStageBytes + (DS_TABLE ? 1024 : 0);
+  // K/V stages, and how far ahead group A loads: INT8 Q smoothing forms a
+  // tile's Delta-S one tile ahead, so it keeps four stages and loads two
+  // tiles ahead
+  constexpr int NS = DS_MFMA ? 4 : 3;
+  constexpr int PD = NS - 2;
+  // INT8 Q smoothing, beyond the stages: per group, Delta-S of two tiles
+  // (by tile parity, 128 ints each), then per group its block's digit rows
+  constexpr int kDsOff = NS * kStage;
+  constexpr int kDigOff = kDsOff + 2048;
   constexpr int NW = 8;
   constexpr int BM = NW * 32;
 
@@ -210,12 +230,40 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 
   v4i qf[4];
   float qscale = 0.0f;
+  // INT8 Q smoothing: the weights of the block's four digit rows (the rows
+  // themselves go to LDS below)
+  float dw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4i dgr[4];  // the digit rows as the A operand, read from LDS once
   if (q0 < p.nbq * 128) {
     const uint8_t* qt = p.q8 + (bh * p.nbq + qblk) * kTileBytes;
     const v4i* src = reinterpret_cast<const v4i*>(qt + ((q0 & 127) + l32) * 128 + 64 * hh);
 #pragma unroll
     for (int m = 0; m < 4; ++m) qf[m] = src[m];
     qscale = p.qs[bh * p.nbq + qblk];
+    if constexpr (DS_MFMA) {
+      const __attribute__((address_space(4))) float* prm =
+          (const __attribute__((address_space(4))) float*)(p.dp) + (bh * p.nbq + qblk) * kDigitParams;
+      qscale = prm[0];  // the block's score unit
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dw[j] = prm[1 + j];
+      const int kshift = __float_as_int(prm[5]);
+      if (kshift > 0) {
+        // a mean of more than 2^15 code units: the unit is qs 2^kshift, and
+        // the codes are rounded to it (half up; 0 from kshift 8 on)
+        const int ksh = min(kshift, 31);
+        const int half = 1 << (ksh - 1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int x = qf[m][j];
+            int y = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y |= ((((int)(int8_t)(x >> (8 * e))) + half) >> ksh & 0xFF) << (8 * e);
+            qf[m][j] = y;
+          }
+      }
+    }
   } else {
 #pragma unroll
     for (int m = 0; m < 4; ++m) qf[m] = v4i{0, 0, 0, 0};
@@ -237,7 +285,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     const uint8_t* src = (c0 < 1024 ? kbase + tile * kTileBytes + c0 * 16
                                     : vbase + tile * kTileBytes + (c0 - 1024) * 16) + lane * 16;
     uint8_t* dst = smem + stage * kStage + c0 * 16;
-    if constexpr (QSMOOTH) {
+    if constexpr (DS_TABLE) {
       // the first copying wave also brings the tile's Delta-S: lanes 0-31
       // the first query block's 128 values, lanes 32-63 the second's
       if (widx == 0) {
@@ -273,8 +321,47 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   const __attribute__((address_space(4))) float* ksc4 =
       (const __attribute__((address_space(4))) float*)(ksc);
 
+  // ---- INT8 Q smoothing: Delta-S of tile u (in LDS stage `stage`) for this
+  // group's query block, keys 32 kb + [0, 32) with kb = w % 4; each of the
+  // group's four waves forms a quarter.  D[r][key] = sum_d a_r[d]
+  // kcode[key][d] on the INT8 MFMA, the digit rows as A (lanes 0-3 of each
+  // half: rows 0-3, channels 64 hh + 16 m + [0, 16) for MFMA m; the other
+  // lanes read zeros) and the keys' codes as B, so lanes 0-31 hold the four
+  // digit sums of key 32 kb + lane in registers 0-3.  Their sum
+  // sum_r 2^(E - 7r) D_r is formed in FP32, rounded to the unit
+  // (|Delta-S| < 2^29) and written to the group's buffer of tile parity
+  // u % 2 (the stage count is even, so that is stage % 2).
+  // ds_digits reads the digit rows (once per sweep), ds_load the keys'
+  // codes, ds_mfma runs the MFMAs, ds_store the sum and the write.
+  auto ds_load = [&](int stage, v4i (&kk)[4]) __attribute__((always_inline)) {
+    const int row = (w & 3) * 32 + l32;
+    const uint8_t* Ks = smem + stage * kStage + row * 128;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kk[m] = *reinterpret_cast<const v4i*>(Ks + ((((4 * hh + m) ^ swz(row)) & 7) << 4));
+  };
+  auto ds_digits = [&](v4i (&dg)[4]) __attribute__((always_inline)) {
+    const uint8_t* dgl = smem + kDigOff + (isA ? 0 : 1024) + (l32 < 4 ? l32 * 128 + 64 * hh : 512);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dg[m] = *reinterpret_cast<const v4i*>(dgl + 16 * m);
+  };
+  auto ds_mfma = [&](const v4i (&kk)[4], const v4i (&dg)[4]) __attribute__((always_inline)) -> v16i {
+    v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(dg[0], kk[0], v16i{}, 0, 0, 0);
+#pragma unroll
+    for (int m = 1; m < 4; ++m) D = __builtin_amdgcn_mfma_i32_32x32x32_i8(dg[m], kk[m], D, 0, 0, 0);
+    return D;
+  };
+  auto ds_store = [&](int stage, const v16i& D) __attribute__((always_inline)) {
+    if (hh == 0) {
+      const float f = __builtin_fmaf((float)D[0], dw[0],
+                                     __builtin_fmaf((float)D[1], dw[1],
+                                                    __builtin_fmaf((float)D[2], dw[2], (float)D[3] * dw[3])));
+      reinterpret_cast<int*>(smem + kDsOff + (isA ? 0 : 1024) + (stage & 1) * 512)[(w & 3) * 32 + l32] =
+          (int)__builtin_rintf(f);
+    }
+  };
+
   // ---- M(t): PV of tile t-1, then S of tile t
-  // kst = t % 3, the LDS stage of tile t.  The steady-state loop passes it
+  // kst = t % NS, the LDS stage of tile t.  The steady-state loop passes it
   // as a literal, so every LDS address is a lane constant plus an immediate.
   // mask_rem < 128 (the partial last tile only): keys at or past mask_rem
   // get the bits of -inf (FP8 Q/K) or the integer minimum (INT8), which the
@@ -288,9 +375,20 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
                     bool mask_all) __attribute__((always_inline)) {
     // the MFMA-issuing wave of the SIMD gets issue priority over its partner
     __builtin_amdgcn_s_setprio(2);
-    if (isA && t >= 1 && t + 1 < nbk) copy_tile(t + 1, kst == 2 ? 0 : kst + 1, w, 4);
+    // tile t+PD comes in halves: group A's waves copy its K tile here, group
+    // B's its V^T tile one slot later (first read two slots after that),
+    // 4 KiB per wave, so that each wave writes M0 once per tile
+    if (t >= 1 && t + PD < nbk) copy_tile(t + PD, (kst + PD) % NS, w, 8);
+    // INT8 Q smoothing: the reads of the operands for the next tile's
+    // Delta-S go ahead of the P.V MFMAs, which hide their latency
+    v4i dsk[4];
+    v16i dsd;
+    const bool ds_more = DS_MFMA && do_s && t + 1 < nbk;
+    if constexpr (DS_MFMA) {
+      if (ds_more) ds_load((kst + 1) % NS, dsk);
+    }
     if (do_pv && !(SPARSE && pv_skip)) {
-      const uint8_t* Vs = smem + (kst == 0 ? 2 : kst - 1) * kStage + kTileBytes;  // stage of t-1
+      const uint8_t* Vs = smem + ((kst + NS - 1) % NS) * kStage + kTileBytes;  // stage of t-1
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const v8i Bp = {(int)P[g][0], (int)P[g][1], (int)P[g][2], (int)P[g][3],
@@ -316,6 +414,30 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     }
     if constexpr (SPARSE) {
       if (do_s) masked_cur = mask_all;
+    }
+    // INT8 Q smoothing: the P.V MFMAs stay ahead of the K operand reads, so
+    // that the V operands and the K operands are never live together (the
+    // empty asm uses O, and no memory access crosses it)
+    if constexpr (DS_MFMA) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) asm volatile("" ::"v"(O[db]) : "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // the next tile's Delta-S MFMAs (summed and stored after the score
+      // MFMAs, off their path), then this tile's Delta-S, the score
+      // accumulators' initial values (register 4a + b of block kb is key
+      // 32 kb + 8a + 4 hh + b; S is free here)
+      if (ds_more) dsd = ds_mfma(dsk, dgr);
+      if (do_s) {
+        const int* dsr = reinterpret_cast<const int*>(smem + kDsOff + (isA ? 0 : 1024) + (kst & 1) * 512);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const v4i d4 = *reinterpret_cast<const v4i*>(dsr + 32 * kb + 8 * a + 4 * hh);
+#pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) S[kb][4 * a + b2] = d4[b2];
+          }
+      }
     }
     if (do_s && !(SPARSE && mask_all)) {
       const uint8_t* Ks = smem + kst * kStage;
@@ -350,6 +472,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      } else if constexpr (DS_MFMA) {
+        // the scores, accumulated onto Delta-S (read at the start of the phase)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][m], qf[m], S[kb], 0, 0, 0);
+        if (ds_more) ds_store((kst + 1) % NS, dsd);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][0], qf[0], v16i{}, 0, 0, 0);
@@ -367,8 +496,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
       }
       // (Q smoothing: a block with qs = 0 has all-zero codes; its scores are
       // the Delta-S table's values, held in units of 2^-20 * ks)
-      c_cur = (QSMOOTH && qscale == 0.0f ? 0x1p-20f : qscale) * ksc4[tile_of(t)] * p.sl2e;
-      if constexpr (QSMOOTH) dstage_cur = kst;
+      c_cur = (DS_TABLE && qscale == 0.0f ? 0x1p-20f : qscale) * ksc4[tile_of(t)] * p.sl2e;
+      if constexpr (DS_TABLE) dstage_cur = kst;
       if (mask_rem < 128) {
         // the first masked key offset of this lane half; the empty asm before
         // each comparison keeps the 64 lane masks from all being computed up
@@ -409,12 +538,11 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     // below their rounding unit) and keeps -inf at -inf.
     const float c = c_cur == 0.0f ? 1.17549435e-38f : c_cur;
     float mt;
-    if constexpr (QSMOOTH) {
+    if constexpr (DS_TABLE) {
       // add Delta-S (in the units of S: the table holds (qmean . kcode) / qs)
       // of this group's query block to every score, written back over S,
-      // then the row maximum on floats; masked keys become -inf.  The INT8
-      // accumulator is converted exactly first, so the sum is rounded once,
-      // at the score's own magnitude.
+      // then the row maximum on floats; masked keys are -inf.  The sum is
+      // rounded once, at the score's own magnitude.
       const float* dsl = reinterpret_cast<const float*>(smem + dstage_cur * kStage + 2 * kTileBytes) +
                          (isA ? 0 : 128) + 4 * hh;
       float mx = -__builtin_inff();
@@ -481,7 +609,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sf = QSMOOTH ? __int_as_float(S[kb][r0 + i]) : score_f(S[kb][r0 + i], masked);
+          const float sf = DS_TABLE ? __int_as_float(S[kb][r0 + i]) : score_f(S[kb][r0 + i], masked);
           pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sf, c, nb));
           // the first term starts the sum (p >= 0, so 0 + p == p)
           ls[i] = (g == 0 && j == 0) ? pv[i] : ls[i] + pv[i];
@@ -519,11 +647,33 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) P[g][j] = 0u;
 
-  // prologue: tiles 0 and 1 into stages 0 and 1, all waves copying
+  // INT8 Q smoothing: the first wave of each group copies its block's four
+  // digit rows (512 bytes; zeros past the last block) into the group's LDS
+  // area, followed by 64 zero bytes, the operand of the A rows 4-31
+  if constexpr (DS_MFMA) {
+    if ((w & 3) == 0) {
+      uint8_t* dst = smem + kDigOff + (isA ? 0 : 1024);
+      uint2 v = make_uint2(0u, 0u);
+      if (q0 < p.nbq * 128) v = reinterpret_cast<const uint2*>(p.dg + (bh * p.nbq + qblk) * kDigitBytes)[lane];
+      reinterpret_cast<uint2*>(dst)[lane] = v;
+      if (lane < 8) reinterpret_cast<uint2*>(dst + 512)[lane] = make_uint2(0u, 0u);
+    }
+  }
+
+  // prologue: tiles 0 .. PD into their stages, all waves copying (INT8 Q
+  // smoothing: then the first tile's Delta-S)
   copy_tile(0, 0, w, 8);
   if (nbk > 1) copy_tile(1, 1, w, 8);
+  if (PD > 1 && nbk > 2) copy_tile(2, 2, w, 8);
   wait_loads();
   __syncthreads();
+  if constexpr (DS_MFMA) {
+    v4i kk[4];
+    ds_digits(dgr);
+    ds_load(0, kk);
+    ds_store(0, ds_mfma(kk, dgr));
+    __syncthreads();
+  }
 
   if (!isA) barrier();  // group B lags one slot
   const int last = nbk - 1;
@@ -535,7 +685,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     mblock(t, do_pv, true, kst, 128, SPARSE && !group_attends(t));
     barrier();
     vblock(!do_pv, false);
-    if (isA) wait_loads();
+    wait_loads();
     barrier();
   };
   int t = 0;
@@ -543,18 +693,27 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     step(0, false, 0);
     t = 1;
   }
-  for (; t + 3 <= last; t += 3) {
-    step(t, true, 1);
-    step(t + 1, true, 2);
-    step(t + 2, true, 0);
+  if constexpr (NS == 4) {
+    for (; t + 4 <= last; t += 4) {
+      step(t, true, 1);
+      step(t + 1, true, 2);
+      step(t + 2, true, 3);
+      step(t + 3, true, 0);
+    }
+  } else {
+    for (; t + 3 <= last; t += 3) {
+      step(t, true, 1);
+      step(t + 1, true, 2);
+      step(t + 2, true, 0);
+    }
   }
-  for (; t < last; ++t) step(t, true, t % 3);
-  mblock(last, last > 0, true, last % 3, rem, SPARSE && !group_attends(last));
+  for (; t < last; ++t) step(t, true, t % NS);
+  mblock(last, last > 0, true, last % NS, rem, SPARSE && !group_attends(last));
   barrier();
   vblock(last == 0, rem < 128);
-  if (isA) wait_loads();
+  wait_loads();
   barrier();
-  mblock(nbk, true, false, nbk % 3, 128, false);
+  mblock(nbk, true, false, nbk % NS, 128, false);
   if (isA) barrier();
 
   // ---- epilogue: O = acc * vs / l448 -> BF16 (or FP32 partials of a split)
@@ -566,8 +725,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
   // ln 2 * (m + log2(l448 / 448)) for the smoothed scores; and (when the
   // caller asked for the LSE) the logit shift the K smoothing removed,
   // softmax_scale * qs * sum_d qc_d kmean_d, from the Q codes this lane
-  // holds (channels 64 hh + [0, 64)).  Split partials carry no shift, so
-  // the merged output does not depend on whether the LSE is asked for.
+  // holds (channels 64 hh + [0, 64); with INT8 Q smoothing qs is the
+  // block's unit and the codes those the scores used).  Split partials
+  // carry no shift, so the merged output does not depend on whether the
+  // LSE is asked for.
   float lse = 0.0f, shift = 0.0f;
   if (p.lse != nullptr || p.splits > 1) lse = kLn2 * (m_run + log2f(lt) - kLog2_448);
   if (p.lse != nullptr) {
@@ -610,12 +771,12 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnP p) {
     // lane holds 4-channel pieces of its row, so direct stores would write
     // 8 bytes into each of 32 rows per instruction; staged, every global
     // store writes whole 128-byte lines (8 lanes per row).  The area is the
-    // stage of the never-loaded tile nbk, whose last reader (tile nbk-3's
-    // PV) is two barriers back.  Chunks are XOR-swizzled by (row >> 1) & 7
+    // stage of the never-loaded tile nbk, whose last reader (tile nbk-NS's
+    // PV) is two barriers back or more.  Chunks are XOR-swizzled by (row >> 1) & 7
     // so the piece writes of 32 rows spread over the banks.  LDS operations
     // of one wave run in order, so the second half's writes land after the
     // first half's reads.
-    uint8_t* obuf = smem + (nbk % 3) * kStage + w * 4096;
+    uint8_t* obuf = smem + (nbk % NS) * kStage + w * 4096;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       // (keeps the compiler from hoisting the second half's scale loads
@@ -746,7 +907,9 @@ template <bool FP8QK, bool SPARSE, bool QSMOOTH>
 hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
   constexpr int BM = 256;
-  constexpr int kLds = 3 * (kStageBytes + (QSMOOTH ? 1024 : 0));
+  // three K/V stages (E4M3 Q smoothing: each with its Delta-S rows); INT8 Q
+  // smoothing: four, then 1 KiB of Delta-S and 1 KiB of digit rows per group
+  constexpr int kLds = QSMOOTH && !FP8QK ? 4 * kStageBytes + 2048 + 2048 : 3 * (kStageBytes + (QSMOOTH ? 1024 : 0));
   // Raising the dynamic LDS limit is per function and device, once each.
   // The flags are atomics: threads that race here may both set the
   // attribute (the same value, harmless), with no unsynchronised access.
@@ -792,7 +955,9 @@ hipError_t launch_pp(const AttnArgs& a, hipStream_t stream) {
   const int64_t G8 = (p.G + 7) / 8 * 8;
   p.lut_counts = a.lut_counts;
   p.lut_entries = a.lut_entries;
-  p.ds = QSMOOTH ? reinterpret_cast<const float*>(a.packed + L.off_ds) : nullptr;
+  p.ds = QSMOOTH && FP8QK ? reinterpret_cast<const float*>(a.packed + L.off_ds) : nullptr;
+  p.dg = QSMOOTH && !FP8QK ? reinterpret_cast<const int8_t*>(a.packed + L.off_dg) : nullptr;
+  p.dp = QSMOOTH && !FP8QK ? reinterpret_cast<const float*>(a.packed + L.off_dp) : nullptr;
   p.qm = QSMOOTH ? reinterpret_cast<const float*>(a.packed + L.off_qm) : nullptr;
   hipLaunchKernelGGL((attn_pp_kernel<FP8QK, SPARSE, QSMOOTH>), dim3((unsigned)G8), dim3(512), kLds, stream, p);
   e = hipGetLastError();

@@ -51,19 +51,28 @@ constexpr int64_t kTileBytes = 128 * 128;
 SATTN_HD inline int64_t nblocks(int64_t n) { return (n + kBlk - 1) / kBlk; }
 SATTN_HD inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Q smoothing, INT8 codes: per Q block, four rows of int8 digits of the
+// block mean over its score unit (kDigitBytes), and the unit, the digits'
+// four weights and the code shift (kDigitParams floats).
+constexpr int64_t kDigitBytes = 4 * 128;
+constexpr int64_t kDigitParams = 8;
+
 struct Layout {
   int64_t B, H, Nq, Nkv, nbq, nbk;
-  bool qsmooth;
-  size_t off_q8, off_k8, off_v8, off_qs, off_ks, off_vs, off_km, off_qm, off_ds, packed_bytes;
+  bool qsmooth, fp8qk;
+  size_t off_q8, off_k8, off_v8, off_qs, off_ks, off_vs, off_km, off_qm, off_ds, off_dg, off_dp, packed_bytes;
   size_t ws_kpart, ws_vpart, workspace_bytes;
 };
 
 // Callers validate sizes first (no overflow for N <= 2^24, B*H <= 2^31, and
-// for Q smoothing the Delta-S section below 2^40 bytes).
-inline Layout make_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, bool qsmooth = false) {
+// for Q smoothing in the FP8 Q/K format the Delta-S section below 2^40
+// bytes).  The sections before the Q means do not depend on the format.
+inline Layout make_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, bool qsmooth = false,
+                          bool fp8qk = false) {
   Layout L;
   L.B = B; L.H = H; L.Nq = Nq; L.Nkv = Nkv;
   L.qsmooth = qsmooth;
+  L.fp8qk = fp8qk;
   L.nbq = nblocks(Nq);
   L.nbk = nblocks(Nkv);
   const size_t bh = (size_t)B * (size_t)H;
@@ -75,10 +84,15 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, bool qs
   L.off_ks = o; o = align256(o + bh * (size_t)L.nbk * 4);
   L.off_vs = o; o = align256(o + bh * kD * 4);
   L.off_km = o; o = align256(o + bh * kD * 4);
-  L.off_qm = L.off_ds = 0;
+  L.off_qm = L.off_ds = L.off_dg = L.off_dp = 0;
   if (qsmooth) {
     L.off_qm = o; o = align256(o + bh * (size_t)L.nbq * kD * 4);
-    L.off_ds = o; o = align256(o + bh * (size_t)L.nbq * (size_t)L.nbk * kBlk * 4);
+    if (fp8qk) {
+      L.off_ds = o; o = align256(o + bh * (size_t)L.nbq * (size_t)L.nbk * kBlk * 4);
+    } else {
+      L.off_dg = o; o = align256(o + bh * (size_t)L.nbq * kDigitBytes);
+      L.off_dp = o; o = align256(o + bh * (size_t)L.nbq * kDigitParams * 4);
+    }
   }
   L.packed_bytes = o;
   size_t w = 0;

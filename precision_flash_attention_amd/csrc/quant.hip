@@ -497,6 +497,8 @@ __global__ __launch_bounds__(256) void k_codes(CodeP p) {
 }
 
 // ------------------------------------------------------------ 4. Delta-S ----
+// With INT8 codes the attention kernel forms Delta-S itself from k_qdigits'
+// digit rows (after this kernel).  The E4M3 Q/K format keeps a table:
 // D[bh][i][t*128 + j] = (q_mean[bh][i] . kcode(t, j)) / u_i for every Q block
 // i, u_i = qs_i (2^-20 when qs_i = 0, a block of equal tokens: its scores
 // are Delta-S alone, kept at FP32 resolution): the score term that restores
@@ -518,12 +520,10 @@ struct DsP {
   const float* q_mean;
   float* ds;
   int64_t nbq, nbk;
-  int fp8qk;
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <bool FP8>
 __global__ __launch_bounds__(256) void k_delta_s(DsP p) {
   const int64_t g = blockIdx.x;  // bh * nbk + t
   const int64_t bh = g / p.nbk, t = g % p.nbk;
@@ -540,15 +540,10 @@ __global__ __launch_bounds__(256) void k_delta_s(DsP p) {
     const int wd[4] = {(int)u.x, (int)u.y, (int)u.z, (int)u.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if constexpr (FP8) {
-        kb[16 * c + 4 * q + 0] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 0);
-        kb[16 * c + 4 * q + 1] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 1);
-        kb[16 * c + 4 * q + 2] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 2);
-        kb[16 * c + 4 * q + 3] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 3);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kb[16 * c + 4 * q + e] = (float)(int8_t)(wd[q] >> (8 * e));
-      }
+      kb[16 * c + 4 * q + 0] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 0);
+      kb[16 * c + 4 * q + 1] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 1);
+      kb[16 * c + 4 * q + 2] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 2);
+      kb[16 * c + 4 * q + 3] = __builtin_amdgcn_cvt_f32_fp8(wd[q], 3);
     }
   }
   const float* qsr = p.q_scale + bh * p.nbq;
@@ -593,6 +588,74 @@ __global__ __launch_bounds__(256) void k_delta_s(DsP p) {
     }
 #pragma unroll
     for (int c = 0; c < 64; ++c) qa[c] = qn[c];
+  }
+}
+
+// Q smoothing with INT8 codes: the block mean in the form the attention
+// kernel multiplies with the K codes on the INT8 MFMA, per (b, h, Q block):
+//   unit  the block's score unit: the accumulator of Qcode . Kcode counts
+//         units of unit * ks.  It is qs, times 2^k when the mean is more
+//         than 2^15 units (then the kernel rounds the Q codes to multiples
+//         of 2^k); for qs = 0 (equal tokens, all-zero codes) amax|mean| * 2^-14.
+//   u_d = mean_d / unit, so |u_d| < 2^15 and, with |Kcode| <= 127, the
+//         correction sum_d u_d Kcode_d and the code product both fit the
+//         accumulator's 32 bits (< 2^29 and <= 2^21);
+//   digit rows a_0..a_3 (int8, |a_r| <= 64) with
+//         u_d = 2^E (a_0 + 2^-7 a_1 + 2^-14 a_2 + 2^-21 a_3) + e_d,
+//         E = ilogb(max_d |u_d|) - 5, |e_d| <= 2^(E-22) (each remainder is
+//         exact in FP32: it is a multiple of the ulp of u_d below 2^24 of them);
+//   params  {unit, 2^E, 2^(E-7), 2^(E-14), 2^(E-21), k (int bits), 0, 0}.
+// One wave per block, two channels per lane; quant.hip is built without FP
+// contraction, so each step is one IEEE operation.
+struct DigP {
+  const float* q_scale;
+  const float* q_mean;
+  int8_t* dg;
+  float* dp;
+  int64_t nblk;
+};
+
+__global__ __launch_bounds__(256) void k_qdigits(DigP p) {
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= p.nblk) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const float2 m2 = reinterpret_cast<const float2*>(p.q_mean + blk * kD)[lane];
+  const float qs = p.q_scale[blk];
+  const float amax = wave_max(fmaxf(fabsf(m2.x), fabsf(m2.y)));
+  int k = 0;
+  float unit;
+  if (qs > 0.0f) {
+    // amax / (qs 2^k) < 2^(ilogb(amax) + 1 - ilogb(qs) - k) <= 2^15
+    if (amax > 0.0f) k = max(0, ilogbf(amax) - ilogbf(qs) - 14);
+    unit = ldexpf(qs, k);
+  } else {
+    unit = amax > 0.0f ? fmaxf(ldexpf(amax, -14), 1.17549435e-38f) : 1.0f;
+  }
+  const float u[2] = {__fdiv_rn(m2.x, unit), __fdiv_rn(m2.y, unit)};
+  const float mu = wave_max(fmaxf(fabsf(u[0]), fabsf(u[1])));
+  const int E = mu > 0.0f ? ilogbf(mu) - 5 : 0;
+  int dig[4][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float r = u[c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // the clamp only acts where the weights underflow (E near -149)
+      const float a = fminf(fmaxf(rintf(ldexpf(r, 7 * j - E)), -127.0f), 127.0f);
+      dig[j][c] = (int)a;
+      r = r - ldexpf(a, E - 7 * j);
+    }
+  }
+  int8_t* dst = p.dg + blk * kDigitBytes + 2 * lane;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<uint16_t*>(dst + 128 * j) = (uint16_t)((dig[j][0] & 0xFF) | ((dig[j][1] & 0xFF) << 8));
+  if (lane < kDigitParams) {
+    float v = 0.0f;
+    if (lane == 0) v = unit;
+    else if (lane <= 4) v = mu > 0.0f ? ldexpf(1.0f, E - 7 * (lane - 1)) : 0.0f;
+    else if (lane == 5) v = __int_as_float(k);
+    p.dp[blk * kDigitParams + lane] = v;
   }
 }
 
@@ -677,12 +740,14 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(k_codes, dim3((unsigned)(BH * (L.nbq + 2 * L.nbk))), dim3(256), 0, stream, cp);
   e = hipGetLastError();
   if (e != hipSuccess || !L.qsmooth) return e;
-  DsP dp{a.packed + L.off_k8, q_scale, q_mean, reinterpret_cast<float*>(a.packed + L.off_ds),
-         L.nbq, L.nbk, a.fp8qk ? 1 : 0};
-  if (a.fp8qk)
-    hipLaunchKernelGGL(k_delta_s<true>, dim3((unsigned)(BH * L.nbk)), dim3(256), 0, stream, dp);
-  else
-    hipLaunchKernelGGL(k_delta_s<false>, dim3((unsigned)(BH * L.nbk)), dim3(256), 0, stream, dp);
+  if (!a.fp8qk) {
+    DigP gp{q_scale, q_mean, reinterpret_cast<int8_t*>(a.packed + L.off_dg),
+            reinterpret_cast<float*>(a.packed + L.off_dp), BH * L.nbq};
+    hipLaunchKernelGGL(k_qdigits, dim3((unsigned)((BH * L.nbq + 3) / 4)), dim3(256), 0, stream, gp);
+    return hipGetLastError();
+  }
+  DsP dp{a.packed + L.off_k8, q_scale, q_mean, reinterpret_cast<float*>(a.packed + L.off_ds), L.nbq, L.nbk};
+  hipLaunchKernelGGL(k_delta_s, dim3((unsigned)(BH * L.nbk)), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 

@@ -176,6 +176,26 @@ def check_rows(o_gpu_bits, o_orc_bits, v_bits, bar_rows, what, min_cos=MIN_COS):
     return ratio, float(e.max()), c
 
 
+def smooth_units(codes):
+    """With Q smoothing and INT8 codes the kernel counts each block's scores
+    in a unit of its own: qs, or qs 2^k with
+    k = max(0, ilogb(amax|qmean|) - ilogb(qs) - 14) when the mean exceeds
+    2^15 code units (the kernel then rounds the codes to multiples of 2^k),
+    or amax|qmean| 2^-14 (at least the smallest normal float; 1 for a zero
+    mean) when qs = 0.  Returns (unit, k), each [B, H, nbq], the units as the
+    kernel's FP32 values."""
+    qs = codes["q_scale"].astype(np.float32)
+    amax = np.abs(codes["q_mean"].astype(np.float32)).max(axis=-1)
+    ilogb = lambda x: np.frexp(x)[1].astype(np.int64) - 1  # noqa: E731
+    pos = qs > 0
+    k = np.where(pos & (amax > 0), np.maximum(0, ilogb(np.where(amax > 0, amax, 1))
+                                              - ilogb(np.where(pos, qs, 1)) - 14), 0)
+    zero_unit = np.where(amax > 0, np.maximum(np.ldexp(amax, -14).astype(np.float32),
+                                              np.float32(1.17549435e-38)), np.float32(1.0))
+    unit = np.where(pos, np.ldexp(qs, k).astype(np.float32), zero_unit).astype(np.float32)
+    return unit.astype(np.float64), k
+
+
 def lse_bar(codes, scale, rows=None) -> np.ndarray:
     """Per-row bar on |lse_gpu - lse_oracle| (natural log), derived from the
     kernel's FP32 steps (u = 2^-24):
@@ -189,8 +209,14 @@ def lse_bar(codes, scale, rows=None) -> np.ndarray:
         once per key tile by an exp2 within 2u: (Nkv + 2 nbk) u;
       - log2, exp2 and the final operations: 2^-20;
     with q~ = |qcode| qs (+ |qmean| with Q smoothing) and k~ = |kcode| ks.
-    The FP8 Q/K format adds the row's delta (fp8_score_error).  [B, H, Nq],
-    or [n] for rows."""
+    The FP8 Q/K format adds the row's delta (fp8_score_error).  With Q
+    smoothing and INT8 codes, Delta-S is rounded to the block's unit (see
+    smooth_units) after a four-digit expansion of qmean / unit (digits below
+    2^-27 amax|qmean| dropped): + (0.5 unit max_j ks_j + 2^-27 amax|qmean|
+    sk) * scale, sk = max_j sum_d |kcode_jd| ks_j; where the codes were
+    rounded to multiples of 2^k, each moved by at most r = min(unit / 2,
+    127 qs): + r (sk + sum_d |kmean_d|) * scale.  [B, H, Nq], or [n] for
+    rows."""
     fmt = codes.get("qk_format", "int8")
     B, H, Nq, _ = codes["q8"].shape
     Nkv = codes["k8"].shape[2]
@@ -198,6 +224,7 @@ def lse_bar(codes, scale, rows=None) -> np.ndarray:
     dec = ((lambda c: np.abs(oracle.e4m3_decode(c.view(np.uint8)))) if fmt == "fp8"
            else (lambda c: np.abs(c.astype(np.float64))))
     out = np.zeros((B, H, Nq)) if rows is None else np.zeros(len(rows))
+    units = smooth_units(codes) if fmt != "fp8" and "q_mean" in codes else None
     for b in range(B):
         for h in range(H):
             if rows is None:
@@ -216,6 +243,15 @@ def lse_bar(codes, scale, rows=None) -> np.ndarray:
                 smag = np.maximum(smag, (qt @ np.ascontiguousarray(kt[j0:j0 + 8192].T)).max(axis=1))
             shift = qt @ np.abs(codes["k_mean"][b, h].astype(np.float64))
             bar = 2.0 ** -17 * (smag + shift) * scale + (Nkv + 2 * nbk) * 2.0 ** -24 + 2.0 ** -20
+            if fmt != "fp8" and "q_mean" in codes:
+                unit, ksh = units[0][b, h][qi // 128], units[1][b, h][qi // 128]
+                ks = codes["k_scale"][b, h].astype(np.float64)
+                sk = (np.abs(codes["k8"][b, h].astype(np.float64)).sum(axis=1) * ks[np.arange(Nkv) // 128]).max()
+                amq = np.abs(codes["q_mean"][b, h][qi // 128].astype(np.float64)).max(axis=1)
+                qsr = codes["q_scale"][b, h][qi // 128].astype(np.float64)
+                r = np.where(ksh > 0, np.minimum(0.5 * unit, 127.0 * qsr), 0.0)
+                kms = np.abs(codes["k_mean"][b, h].astype(np.float64)).sum()
+                bar = bar + (0.5 * unit * ks.max() + 2.0 ** -27 * amq * sk + r * (sk + kms)) * scale
             if sel is None:
                 out[b, h] = bar
             else:

@@ -323,19 +323,23 @@ def test_product_does_not_reference_the_oracle():
 
 
 def test_q_smoothing_sizes_and_flags(lib):
-    # the option adds the block means and the Delta-S table
+    # the option adds the block means; then, with INT8 codes, four int8 digit
+    # rows and 8 parameters per Q block, and with E4M3 codes the Delta-S table
     B, H, Nq, Nkv = 2, 3, 300, 700
     base = sattn.packed_bytes(B, H, Nq, Nkv)[0]
     nbq, nbk = 3, 6
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = base + a(B * H * nbq * 128 * 4) + a(B * H * nbq * nbk * 128 * 4)
-    assert sattn.packed_bytes(B, H, Nq, Nkv, q_smooth=True)[0] == want
-    assert sattn.packed_bytes(B, H, Nq, Nkv, qk_format="fp8", q_smooth=True)[0] == want
+    means = a(B * H * nbq * 128 * 4)
+    assert (sattn.packed_bytes(B, H, Nq, Nkv, q_smooth=True)[0]
+            == base + means + a(B * H * nbq * 512) + a(B * H * nbq * 8 * 4))
+    assert (sattn.packed_bytes(B, H, Nq, Nkv, qk_format="fp8", q_smooth=True)[0]
+            == base + means + a(B * H * nbq * nbk * 128 * 4))
     pb = ctypes.c_size_t()
     assert lib.sattn_packed_bytes_ex(1, 2, 256, 256, 128, 0x20, ctypes.byref(pb), None) == INVALID
     assert lib.sattn_packed_bytes_ex(1, 2, 256, 256, 128, 0x12, ctypes.byref(pb), None) == INVALID
-    # Delta-S beyond 2^40 bytes is refused
-    assert lib.sattn_packed_bytes_ex(1, 1 << 8, 1 << 24, 1 << 17, 128, 0x10, ctypes.byref(pb), None) == UNSUPPORTED
+    # a Delta-S table beyond 2^40 bytes is refused; the INT8 form has none
+    assert lib.sattn_packed_bytes_ex(1, 1, 1 << 24, 1 << 24, 128, 0x11, ctypes.byref(pb), None) == UNSUPPORTED
+    assert lib.sattn_packed_bytes_ex(1, 1, 1 << 24, 1 << 24, 128, 0x10, ctypes.byref(pb), None) == OK
     st = strides(65536, 256, 128)
     small = sattn.packed_bytes(1, 2, 256, 256)[0]   # enough without smoothing only
     assert lib.sattn_quantize_qkv_ex(ALIGNED, ALIGNED, ALIGNED, 1, 2, 256, 256, 128, st, None, None, 0x10,

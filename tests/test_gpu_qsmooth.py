@@ -115,6 +115,27 @@ def test_q_with_mean_offset(device, fmt):
     assert e1 < 0.9 * e0
 
 
+def _bf16(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_degenerate_blocks(device, fmt):
+    # Q block 1: 128 equal tokens (qs = 0, all-zero codes: the scores are
+    # the block mean's alone); block 2: one channel at 3000 over a residual
+    # of about 1e-3 (a mean of ~1e8 code units, past the INT8 accumulator
+    # unless counted in a coarser unit); block 0 ordinary
+    rng = np.random.default_rng(31)
+    H, Nq, Nkv = 2, 300, 400
+    q = rng.normal(size=(1, Nq, H, 128)).astype(np.float32)
+    q[:, 128:256] = rng.normal(size=(1, 1, H, 128))
+    q[:, 256:] = rng.normal(0.0, 1e-3, size=(1, Nq - 256, H, 128))
+    q[:, 256:, :, 0] = 3000.0
+    _, k, v = testkit.make_inputs(testkit.CONFIGS[4], seed=32, H=H, Nq=Nq, Nkv=Nkv)
+    check(_bf16(q), k, v, "degenerate Q blocks", fmt)
+
+
 @pytest.mark.parametrize("num_splits", [3, 0])
 def test_split_kv(device, num_splits):
     cfg = testkit.CONFIGS[4]
