@@ -88,8 +88,9 @@ bool valid_format(int f) {
 bool is_fp8(int f) { return (f & ~SATTN_QK_SMOOTH_Q) == SATTN_QK_FP8; }
 bool is_qsmooth(int f) { return (f & SATTN_QK_SMOOTH_Q) != 0; }
 
-// Q smoothing adds a Delta-S table of B*H*nbq*nbk*128 floats; past 2^40
-// bytes (far beyond device memory) the sizes are refused.
+// Q smoothing in the E4M3 Q/K format adds a Delta-S table of
+// B*H*nbq*nbk*128 floats; past 2^40 bytes (far beyond device memory) the
+// sizes are refused.
 sattn_status check_qsmooth(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int f) {
   if (!is_qsmooth(f) || !is_fp8(f)) return SATTN_OK;
   const double bytes = (double)B * (double)H * (double)sattn::nblocks(Nq) * (double)sattn::nblocks(Nkv) * 512.0;
