@@ -139,10 +139,13 @@ __device__ inline void copy_to_lds_off(const uint8_t* src_lane, uint8_t* dst_wav
 
 // NBK: key tiles of a head (1..4), a template parameter so that every tile's
 // LDS addresses are lane constants plus immediates.  LSE: the per-row LSE is
-// written too (the instances without it carry none of its code).
+// written too (the instances without it carry none of its code).  TAIL: the
+// last key tile is partial (Nkv not a multiple of 128); without it the
+// instance carries no masking code, whose registers would otherwise be
+// reserved across the whole tile loop.
 // One run of a workgroup: query tiles [t_lo, t_hi) of head bh, with the
 // head's K and V^T loaded into LDS first.
-template <bool FP8QK, int NBK, bool LSE>
+template <bool FP8QK, int NBK, bool LSE, bool TAIL>
 __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p, const int64_t bh, const int t_lo,
                                                                 const int t_hi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -481,7 +484,10 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
           pvv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(score_f(S[kb][r0 + i]), c, nb));
           ls[i] = (g == 0 && j == 0) ? pvv[i] : ls[i] + pvv[i];
         }
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pvv[0], pvv[1], 0, false);
+        // the first conversion writes the low half only: start from the
+        // register's old contents instead of materialising a zero (not in
+        // the instances with a partial tile, where holding them costs spills)
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pvv[0], pvv[1], TAIL ? 0 : (int)P[g][j], false);
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(pvv[2], pvv[3], wd, true);
         P[g][j] = (uint32_t)wd;
       }
@@ -538,7 +544,9 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
     for (int t = 0; t < NBK; ++t) {
       // M phase
       __builtin_amdgcn_s_setprio(2);
-      const bool masked = t == NBK - 1 && rem < 128;
+      // (TAIL implies rem < 128; the run-time test keeps the masking code in
+      // a branch of its own, which in the one-tile instances avoids spills)
+      const bool masked = TAIL && t == NBK - 1 && rem < 128;
       if (t > 0) {
         pv(t - 1);
         scores(t, masked, t == NBK - 1);
@@ -602,7 +610,7 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
 // The B*H*mt query tiles, in head order, are cut into p.groups equal
 // contiguous shares, one per workgroup (one workgroup per CU); a share that
 // spans heads is run head by head, reloading K and V^T in between.
-template <bool FP8QK, int NBK, bool LSE>
+template <bool FP8QK, int NBK, bool LSE, bool TAIL>
 __global__ __launch_bounds__(512, 1) void attn_short_kernel(ShortP p) {
   // the first p.extra workgroups take p.share + 1 tiles, the rest p.share
   const int g = blockIdx.x;
@@ -616,7 +624,7 @@ __global__ __launch_bounds__(512, 1) void attn_short_kernel(ShortP p) {
     // the previous run's reads of the K/V^T and staging areas are complete
     // before this run's copies overwrite them
     if (!first) __syncthreads();
-    short_run<FP8QK, NBK, LSE>(p, bh, t_lo, t_hi);
+    short_run<FP8QK, NBK, LSE, TAIL>(p, bh, t_lo, t_hi);
     lo += t_hi - t_lo;
   }
 }
@@ -634,7 +642,7 @@ int cu_count() {
   return v;
 }
 
-template <bool FP8QK, int NBK, bool LSE>
+template <bool FP8QK, int NBK, bool LSE, bool TAIL>
 hipError_t launch_short(const AttnArgs& a, hipStream_t stream) {
   const Layout& L = a.L;
   constexpr int kMaxDev = 64;
@@ -643,7 +651,7 @@ hipError_t launch_short(const AttnArgs& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDev || !attr_set[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_short_kernel<FP8QK, NBK, LSE>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_short_kernel<FP8QK, NBK, LSE, TAIL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDev) attr_set[dev].store(true, std::memory_order_release);
@@ -676,7 +684,7 @@ hipError_t launch_short(const AttnArgs& a, hipStream_t stream) {
   p.scale = a.softmax_scale;
   p.sl2e = a.softmax_scale * kLog2e;
   const int64_t grid = groups;
-  hipLaunchKernelGGL((attn_short_kernel<FP8QK, NBK, LSE>), dim3((unsigned)grid), dim3(512), kLds, stream, p);
+  hipLaunchKernelGGL((attn_short_kernel<FP8QK, NBK, LSE, TAIL>), dim3((unsigned)grid), dim3(512), kLds, stream, p);
   return hipGetLastError();
 }
 
@@ -692,21 +700,27 @@ bool short_kv_applies(const AttnArgs& a) {
          a.L.B * a.L.H * ((a.L.Nq + 255) / 256) > (int64_t)cu_count();
 }
 
-template <bool FP8QK, bool LSE>
+template <bool FP8QK, bool LSE, bool TAIL>
 hipError_t launch_short_nbk(const AttnArgs& a, hipStream_t stream) {
   switch (a.L.nbk) {
-    case 1: return launch_short<FP8QK, 1, LSE>(a, stream);
-    case 2: return launch_short<FP8QK, 2, LSE>(a, stream);
-    case 3: return launch_short<FP8QK, 3, LSE>(a, stream);
-    case 4: return launch_short<FP8QK, 4, LSE>(a, stream);
+    case 1: return launch_short<FP8QK, 1, LSE, TAIL>(a, stream);
+    case 2: return launch_short<FP8QK, 2, LSE, TAIL>(a, stream);
+    case 3: return launch_short<FP8QK, 3, LSE, TAIL>(a, stream);
+    case 4: return launch_short<FP8QK, 4, LSE, TAIL>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <bool FP8QK, bool LSE>
+hipError_t launch_short_tail(const AttnArgs& a, hipStream_t stream) {
+  return a.L.Nkv % 128 != 0 ? launch_short_nbk<FP8QK, LSE, true>(a, stream)
+                            : launch_short_nbk<FP8QK, LSE, false>(a, stream);
+}
+
 hipError_t launch_attention_short(const AttnArgs& a, hipStream_t stream) {
   if (a.lse != nullptr)
-    return a.fp8qk ? launch_short_nbk<true, true>(a, stream) : launch_short_nbk<false, true>(a, stream);
-  return a.fp8qk ? launch_short_nbk<true, false>(a, stream) : launch_short_nbk<false, false>(a, stream);
+    return a.fp8qk ? launch_short_tail<true, true>(a, stream) : launch_short_tail<false, true>(a, stream);
+  return a.fp8qk ? launch_short_tail<true, false>(a, stream) : launch_short_tail<false, false>(a, stream);
 }
 
 }  // namespace sattn

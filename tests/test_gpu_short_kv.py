@@ -24,13 +24,16 @@ def maxv(v):
 
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])
 @pytest.mark.parametrize("B,H,Nq,Nkv", [(1, 11, 16300, 300), (1, 8, 16384, 256), (2, 9, 7000, 77),
-                                        (1, 300, 100, 200), (1, 290, 200, 512)])
+                                        (1, 300, 100, 200), (1, 290, 200, 512), (1, 8, 16384, 128),
+                                        (1, 12, 9000, 384)])
 def test_full_output_and_lse(device, fmt, B, H, Nq, Nkv):
     # (1, 11, 16300, 300): Q tail of 172 rows (the last 256-query tile's
     # second block holds 44), K tail of 44 keys; (1, 8, 16384, 256): exact;
     # (2, 9, 7000, 77): one key tile, 77 keys; (1, 300, 100, 200): one query
     # tile per head, its second Q block absent; (1, 290, 200, 512): one
-    # ragged query tile per head against four full key tiles.
+    # ragged query tile per head against four full key tiles; (1, 8, 16384,
+    # 128) and (1, 12, 9000, 384): one and three full key tiles.  Key counts
+    # that are multiples of 128 run the instances without tail masking.
     q, k, v = testkit.make_inputs(testkit.CONFIGS[3], seed=31 + H, B=B, H=H, Nq=Nq, Nkv=Nkv)
     p = sattn.quantize_qkv(to_dev(q), to_dev(k), to_dev(v), qk_format=fmt)
     o, lse = sattn.fwd_cross(p, SCALE, return_lse=True)
