@@ -6,6 +6,7 @@ import time
 
 import numpy as np
 
+import fp8_mfma_model
 import oracle
 import testkit
 
@@ -108,19 +109,16 @@ FULL_SIZE_STRIDE = {3: 32, 4: 32, 5: 128}
 
 # FP8 Q/K format: v_mfma_scale_f32_32x32x64_f8f6f4 does not return the
 # correctly rounded sum of its products (the INT8 instruction is exact).
-# Its error is bounded here by FP8_DOT_REL times the sum of the products'
-# magnitudes; a score error of at most delta_i (natural-log units) on row i
-# moves that row's output by at most 2 delta_i max|V| to first order.
-FP8_DOT_REL = 2.0 ** -11
-
-
+# fp8_mfma_model states how it sums them and bounds the score error per
+# (query, key) from the codes; a score error of at most delta_i (natural-log
+# units) on row i moves that row's output by at most 2 delta_i max|V| to
+# first order.
 def fp8_score_error(codes, scale, rows=None) -> np.ndarray:
-    """delta per query row: FP8_DOT_REL * max_j sum_d |q_id k_jd| qs_i ks_j
-    * softmax_scale, from the oracle's codes.  [B, H, Nq], or [n] for
-    rows[:, (b, h, i)]."""
+    """delta per query row: max_j of the model's dot-product error bound for
+    (q_i, k_j) in code units, times qs_i ks_j softmax_scale, from the
+    oracle's codes.  [B, H, Nq], or [n] for rows[:, (b, h, i)]."""
     B, H, Nq, _ = codes["q8"].shape
     Nkv = codes["k8"].shape[2]
-    dec = lambda c: np.abs(oracle.e4m3_decode(c.view(np.uint8)))  # noqa: E731
     out = np.zeros((B, H, Nq)) if rows is None else np.zeros(len(rows))
     for b in range(B):
         for h in range(H):
@@ -132,12 +130,14 @@ def fp8_score_error(codes, scale, rows=None) -> np.ndarray:
                 if sel.size == 0:
                     continue
                 qi = rows[sel, 2]
-            qa = dec(codes["q8"][b, h, qi]) * codes["q_scale"][b, h][qi // 128].astype(np.float64)[:, None]
-            ka = dec(codes["k8"][b, h]) * codes["k_scale"][b, h][np.arange(Nkv) // 128].astype(np.float64)[:, None]
+            qc = codes["q8"][b, h, qi].view(np.uint8)
+            kc = codes["k8"][b, h].view(np.uint8)
+            ks = codes["k_scale"][b, h][np.arange(Nkv) // 128].astype(np.float64)
             worst = np.zeros(len(qi))
             for j0 in range(0, Nkv, 8192):
-                worst = np.maximum(worst, (qa @ np.ascontiguousarray(ka[j0:j0 + 8192].T)).max(axis=1))
-            d = FP8_DOT_REL * worst * scale
+                e = fp8_mfma_model.dot_error_bound(qc, kc[j0:j0 + 8192]) * ks[None, j0:j0 + 8192]
+                worst = np.maximum(worst, e.max(axis=1))
+            d = worst * codes["q_scale"][b, h][qi // 128].astype(np.float64) * scale
             if sel is None:
                 out[b, h] = d
             else:
