@@ -17,7 +17,9 @@
 //   - the two wave groups' MFMA / softmax alternation (see attn_fwd.hip)
 //     runs on without a break from one query tile to the next: the MFMA
 //     phase that finishes a tile's last P.V also starts the next tile's
-//     Q.K^T and, between those MFMAs, writes the finished tile's output;
+//     Q.K^T and, between those MFMAs, writes half of the finished tile's
+//     output; the next softmax phase, the tile's first (no rescale), writes
+//     the other half;
 //   - each wave's next Q codes are copied into LDS a whole query tile ahead.
 // LDS: the K tiles (16 KiB each) in the first 64 KiB, the V^T tiles in the
 // next 64 KiB, and 4 KiB per wave to stage its Q codes and output rows:
@@ -278,9 +280,12 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
   // can interleave with the Q.K^T MFMAs issued before it.  (The arithmetic
   // runs before the first tile too, so that the P.V products it consumes
   // are not sunk into a conditional block.)
-  auto epilogue = [&](int mt, float shift, bool write) __attribute__((always_inline)) {
+  // Halves [h_lo, h_hi) of the rows' channels (half h: O blocks 2h, 2h+1);
+  // inv = 1 / l448 of the rows, taken before the next tile resets l.  The
+  // LSE goes out with half 0, while m and l are still the tile's.
+  auto epilogue = [&](int mt, float shift, bool write, int h_lo, int h_hi, float inv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(O[db]));
+    for (int db = 2 * h_lo; db < 2 * h_hi; ++db) asm volatile("" : "+v"(O[db]));
     const int q0 = mt * 256 + w * 32;
     const int ln = fresh_lane(), el32 = ln & 31, ehh = ln >> 5;
     // the staging area's rows go out as 16-byte chunks: lane ln stores chunk
@@ -293,10 +298,8 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
     const __amdgpu_buffer_rsrc_t orsrc =
         uniform_rsrc(fresh_s(outh) + (int64_t)q0 * os1f, nrows > 0 ? (nrows - 1) * rb + 256 : 0);
     const int ooff = rr * rb + 16 * cc;
-    const float lt = l_run + other_half_f(l_run);
-    const float inv = 1.0f / lt;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = h_lo; half < h_hi; ++half) {
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int db2 = 0; db2 < 2; ++db2) {
@@ -323,7 +326,8 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_buffer_store_b128(val[i], orsrc, ooff + 8 * i * rb + 128 * half, 0, 0);
     }
-    if constexpr (LSE) {
+    if (LSE && h_lo == 0) {
+      const float lt = l_run + other_half_f(l_run);
       // the LSE of row el32 from the lanes of half 0 (the others' offset is
       // past the range)
       const __amdgpu_buffer_rsrc_t lrsrc = uniform_rsrc(lseh + q0, 4 * nrows);
@@ -539,6 +543,7 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
   // the ping-pong over query tiles and their key tiles; group B runs one
   // barrier slot behind group A
   if (!isA) barrier();
+  float shift_prev = 0.0f, inv_prev = 0.0f;
   for (int mt = t_lo; mt < t_hi; ++mt) {
 #pragma unroll
     for (int t = 0; t < NBK; ++t) {
@@ -554,11 +559,12 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
         if (LSE && t == NBK - 1) shift = lse_shift();
       } else {
         // the previous query tile's last P.V (P = 0 before the first tile)
-        // and this tile's first S; then, while those MFMAs run, the previous
-        // tile's output through the staging area and the next tile's codes
-        // into it
+        // and this tile's first S; then, while those MFMAs run, the first
+        // half of the previous tile's output through the staging area (the
+        // second half follows in this tile's first softmax phase, which has
+        // no rescale to do)
         pv(NBK - 1);
-        float shift_prev = shift;
+        shift_prev = shift;
         if constexpr (NBK == 1) {
           // (one key tile: this tile's codes are read here)
           if (LSE && mt > t_lo) shift_prev = lse_shift();
@@ -571,16 +577,16 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
         for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(O[db]));
         __builtin_amdgcn_sched_barrier(0);
         scores(0, masked, false);
-        epilogue(mt - 1, shift_prev, mt > t_lo);
+        inv_prev = 1.0f / (l_run + other_half_f(l_run));
+        epilogue(mt - 1, shift_prev, mt > t_lo, 0, 1, inv_prev);
         // a wave issues in order: each Q.K^T MFMA followed by a share of the
         // output's VALU work, which then runs while the MFMA does
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (mt + 1 < t_hi) qvalid = q_dma(mt + 1);
         reset();
       }
       // The phase's MFMAs are issued before the barrier: without these uses
@@ -594,8 +600,14 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
       __builtin_amdgcn_s_setprio(0);
       barrier();
       // V phase (with two key tiles or more, the last one first reads the
-      // next query tile's codes, copied into the staging area a tile ago)
+      // next query tile's codes, copied into the staging area a tile ago;
+      // the first one writes the second half of the previous tile's output,
+      // then starts the copy of the next tile's codes into the staging area)
       if (NBK > 1 && t == NBK - 1 && mt + 1 < t_hi) q_read(mt + 1, qvalid);
+      if (t == 0) {
+        epilogue(mt - 1, shift_prev, mt > t_lo, 1, 2, inv_prev);
+        if (mt + 1 < t_hi) qvalid = q_dma(mt + 1);
+      }
       vblock(t == 0, masked);
       barrier();
     }
@@ -603,7 +615,7 @@ __device__ __attribute__((always_inline)) inline void short_run(const ShortP& p,
   // the last query tile's P.V and output
   pv(NBK - 1);
   if constexpr (LSE && NBK == 1) shift = lse_shift();
-  epilogue(t_hi - 1, shift, true);
+  epilogue(t_hi - 1, shift, true, 0, 2, 1.0f / (l_run + other_half_f(l_run)));
   if (isA) barrier();
 }
 
