@@ -36,19 +36,31 @@ TRUNC_REL = 7.0 * 2.0 ** -KEEP_BITS
 SUM_REL = 2.0 ** -19
 
 
-def e4m3_value(codes) -> np.ndarray:
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _value_table() -> np.ndarray:
+    c = np.arange(256, dtype=np.int64)
     e = (c >> 3) & 0xF
     m = c & 7
-    v = np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e - 10))
+    v = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, e - 10))
     return np.where(c & 0x80, -v, v)
+
+
+_VALUE = _value_table()
+_EXPONENT = np.where(((np.arange(256) >> 3) & 0xF) == 0, -6, ((np.arange(256) >> 3) & 0xF) - 7)
+
+
+def e4m3_value(codes) -> np.ndarray:
+    return _VALUE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_magnitudes() -> np.ndarray:
+    """|value| of every code byte, for table lookups."""
+    return np.abs(_VALUE)
 
 
 def e4m3_exponent(codes) -> np.ndarray:
     """The exponent the alignment uses: e - 7 for normal codes, -6 for
     subnormal ones (zero codes included; callers mask them)."""
-    e = (np.asarray(codes, dtype=np.uint8).astype(np.int64) >> 3) & 0xF
-    return np.where(e == 0, -6, e - 7)
+    return _EXPONENT[np.asarray(codes, dtype=np.uint8)]
 
 
 def model_dot(a_codes, b_codes, acc=0.0):
@@ -72,18 +84,17 @@ def model_dot(a_codes, b_codes, acc=0.0):
     return total, float(np.float32(total))
 
 
+def group_weights(codes) -> np.ndarray:
+    """2^EG per row and group of 8 channels, EG the largest exponent of the
+    group's nonzero codes (0 for a group without any): [n, D / 8]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    e = np.where((c & 0x7F) != 0, e4m3_exponent(c), -1000).reshape(c.shape[0], -1, GROUP).max(axis=2)
+    return np.where(e > -1000, np.ldexp(1.0, np.maximum(e, -60)), 0.0)
+
+
 def group_exponent_sum(q_codes, k_codes) -> np.ndarray:
-    """sum_g 2^(EQ_g + EK_g) for every (row of q, row of k): [n, m].  EQ_g is
-    the largest exponent of the nonzero codes in channels 8g .. 8g + 7 (a
-    group without any contributes 0)."""
-    q = np.asarray(q_codes, dtype=np.uint8)
-    k = np.asarray(k_codes, dtype=np.uint8)
-    nz = lambda c: (c & 0x7F) != 0  # noqa: E731
-    eq = np.where(nz(q), e4m3_exponent(q), -1000).reshape(q.shape[0], -1, GROUP).max(axis=2)
-    ek = np.where(nz(k), e4m3_exponent(k), -1000).reshape(k.shape[0], -1, GROUP).max(axis=2)
-    wq = np.where(eq > -1000, np.ldexp(1.0, np.maximum(eq, -60)), 0.0)
-    wk = np.where(ek > -1000, np.ldexp(1.0, np.maximum(ek, -60)), 0.0)
-    return wq @ wk.T
+    """sum_g 2^(EQ_g + EK_g) for every (row of q, row of k): [n, m]."""
+    return group_weights(q_codes) @ group_weights(k_codes).T
 
 
 def dot_error_bound(q_codes, k_codes) -> np.ndarray:
@@ -91,4 +102,4 @@ def dot_error_bound(q_codes, k_codes) -> np.ndarray:
     row): [n, m]."""
     qa = np.abs(e4m3_value(q_codes))
     ka = np.abs(e4m3_value(k_codes))
-    return TRUNC_REL * group_exponent_sum(q_codes, k_codes) + SUM_REL * (qa @ ka.T)
+    return TRUNC_REL * group_exponent_sum(q_codes, k_codes) + SUM_REL * (qa @ np.ascontiguousarray(ka.T))
